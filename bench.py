@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of one PCP prefill step on one MI355X.
+
+A step is the whole hot path on one batch: pcp_partition, pcp_kv_insert for every
+virtual rank, mla_prefill_partial for every virtual rank (one after another, each at
+its real shape), and pcp_lse_merge. Default workload: one 131072-token request, P = 4,
+16 heads, latent 512 + rope 64 (bf16), per-head sink.
+
+Prints ONE JSON line. ``value`` is the attention TFLOP/s of the whole step
+(algorithmic flops of all ranks' partials / wall time of the step, inputs resident in
+HBM). ``roofline`` covers the dominant kernel (the partial attention), with its
+average launch time from HIP events on the launch stream. ``cpu_baseline`` times the
+fp64 oracle on a bounded sample of query rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+
+
+def attn_flops(positions: np.ndarray, H: int, Dl: int, Dr: int) -> float:
+    """Algorithmic flops of causal MLA attention: 2*(Dqk + Dv) per (query, head, key)."""
+    return float(2 * (Dl + Dr + Dl) * H) * float((positions.astype(np.int64) + 1).sum())
+
+
+def merge_bytes(merge_src: np.ndarray, H: int, Dv: int) -> float:
+    """Bytes the merge must move: each contributor row (O bf16 + LSE fp32) read, each
+    output row written, plus the map."""
+    n_contrib = int((merge_src >= 0).sum())
+    T, P = merge_src.shape
+    return float(n_contrib * H * (2 * Dv + 4) + T * H * (2 * Dv + 4) + T * P * 4)
+
+
+def cpu_baseline(w, n_tokens: int, seconds: float):
+    """Time the oracle on a bounded sample of query tokens (their full key sets)."""
+    from oracle import attention as oa
+    from oracle import numerics as on
+    from oracle import partition as op
+    from context_mla_prefill_amd import synth
+
+    plan = op.partition(w.q_lens, w.kv_lens, w.kv_start, w.P)
+
+    rng = np.random.default_rng(12345)
+    pos_all = np.concatenate([rp.positions for rp in plan.ranks])
+    gid_all = np.concatenate([rp.local_gidx for rp in plan.ranks])
+    pos = np.full(plan.T_glob, -1, np.int64)
+    pos[gid_all] = pos_all
+    toks = np.sort(rng.choice(plan.T_glob, size=min(n_tokens, plan.T_glob), replace=False))
+    n_keys = int(pos[toks].max()) + 1
+    lat = on.bf16_to_f64(synth.latent_rows(w, 0, n_keys))
+    rope = on.bf16_to_f64(synth.rope_rows(w, 0, n_keys))
+    sink = synth.sink(w).astype(np.float64)
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    for t in toks:
+        qt = on.bf16_to_f64(synth.q_rows(w, int(t), int(t) + 1))
+        oa.dense_causal_block(qt, pos[[t]], lat, rope, float(w.scale), sink)
+        done += 1
+        flops += 2.0 * (w.Dl + w.Dr + w.Dl) * w.H * (pos[t] + 1)
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} random query tokens of the workload (all {w.H} heads, full causal key sets, "
+                      f"fp64), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the virtual PCP ranks run "
+              "one after another on that GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from context_mla_prefill_amd import _lib, synth
+    from context_mla_prefill_amd import pipeline as pp
+
+    _lib.load()
+    w = synth.workload(args.workload)
+    if w.topk:
+        raise SystemExit("the sparse workload is not wired into bench.py yet")
+    dev = "cuda"
+
+    def upload(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_setup = time.perf_counter()
+    q = upload(synth.q_rows(w))
+    lat_full = upload(synth.latent_rows(w))
+    rope_full = upload(synth.rope_rows(w))
+    sink = torch.from_numpy(synth.sink(w)).to(dev)
+    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+    pp.run_partition(pl)
+    ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full) for r in range(w.P)]
+    del q
+    kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
+    kv_rope = rope_full.clone()
+    bufs = pp.alloc_step(pl, w.H, w.Dl)
+    args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale)
+              for r in range(w.P)]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    stream = torch.cuda.current_stream()
+    n_ev = w.P + 1
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+              for _ in range(args.steps)]
+
+    def step(ev=None):
+        pp.run_partition(pl)
+        for r in range(w.P):
+            _lib.pcp_kv_insert(ranks[r].latent, ranks[r].rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
+                               _lib.MLA_KV_BF16, w.N_kv, kv_lat, kv_rope)
+        for r in range(w.P):
+            if ev:
+                ev[r][0].record(stream)
+            _lib.mla_prefill_partial(args_r[r])
+            if ev:
+                ev[r][1].record(stream)
+        if ev:
+            ev[w.P][0].record(stream)
+        pp.run_merge(pl, bufs, sink, w.H, w.Dl)
+        if ev:
+            ev[w.P][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+
+    # algorithmic work from the device plan's own positions
+    pos_r = [pl.positions[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
+    flops_r = [attn_flops(p, w.H, w.Dl, w.Dr) for p in pos_r]
+    flops_step = float(sum(flops_r))
+    t_rank = [float(np.mean([events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)]))
+              for r in range(w.P)]
+    t_merge = float(np.mean([events[k][w.P][0].elapsed_time(events[k][w.P][1]) for k in range(args.steps)]))
+    avg_launch_ms = float(np.mean(t_rank))
+    achieved = (flops_step / w.P) / (avg_launch_ms * 1e-3) / 1e12
+    mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl)
+
+    out = {
+        "metric": "PCP-shard MLA prefill attention TFLOP/s + MFMA% at 1 GPU; merge GB/s",
+        "value": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 bf16 q/latent/rope, N(0,1) sink)",
+        "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
+                   "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "attention": {"rank_ms": [round(x, 3) for x in t_rank],
+                      "rank_tflops": [round(f / (t * 1e-3) / 1e12, 2) for f, t in zip(flops_r, t_rank)],
+                      "balance_last_over_first": round(t_rank[-1] / t_rank[0], 4),
+                      "tokens_per_s": round(w.T_glob / (ms_step * 1e-3), 1)},
+        "merge": {"ms": round(t_merge, 4), "GB/s": round(mbytes / (t_merge * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(mbytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": mbytes},
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, 64, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

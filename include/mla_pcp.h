@@ -1,0 +1,201 @@
+/*
+ * mla_pcp.h — C ABI of the MI355X (gfx950) library for prefill-context-parallel (PCP)
+ * MLA prefill attention: DualChunkSwap partition, all-gather stand-in KV insert,
+ * rank-local causal (or top-k sparse) partial attention, and the log-sum-exp merge
+ * that applies the per-head attention sink once.
+ *
+ * Conventions for every call below
+ *  - Plain pointers and sizes only. "device" pointers are HIP device memory (or
+ *    managed memory visible to the GPU); "host" pointers are ordinary host memory.
+ *  - Every buffer is owned by the caller. No call allocates, frees or retains memory;
+ *    the only library state is a thread-local error string.
+ *  - Calls that take `stream` (a hipStream_t; NULL = the null stream) only enqueue
+ *    work and return without synchronising. Inputs must stay unchanged until the
+ *    stream reaches the work.
+ *  - Layouts are row-major and contiguous; integer indices are int32; bf16 is the
+ *    IEEE binary32 top half; fp8 is OCP E4M3FN.
+ *  - Arguments are validated on the host before any launch. On a non-OK status
+ *    nothing was enqueued (except MLA_ERR_HIP, which reports a failed launch) and
+ *    mla_pcp_last_error() describes the problem. No call aborts or throws.
+ *  - Kernels bound every memory access by the sizes passed in, so device data that
+ *    breaks a stated precondition gives wrong values, never an out-of-bounds access.
+ */
+#ifndef MLA_PCP_H
+#define MLA_PCP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_PCP_ABI_VERSION 1
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1, /* null pointer, bad or inconsistent size, misalignment */
+    MLA_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement     */
+    MLA_ERR_HIP = 3          /* the HIP runtime reported an error                    */
+} mla_status;
+
+/* KV element types */
+#define MLA_KV_BF16 0
+#define MLA_KV_FP8_E4M3 1 /* latent only; rope stays bf16; one fp32 scale per 64 rows */
+
+/* Library ABI version (MLA_PCP_ABI_VERSION of the build). */
+int mla_pcp_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* mla_pcp_last_error(void);
+
+/*
+ * pcp_plan_sizes — host-only sizing of a DualChunkSwap plan.
+ * Source: "[Core] Add MRV2 virtual-batch PCP for MLA", "PCP algorithm" and
+ * "DualChunkSwap partitioning": each prefill is split on its own into 2*P chunks and
+ * rank r receives chunks r and 2P-1-r; decode rows are replicated on every rank.
+ * A request with q_len < 2P (decode rows, short prefills) is replicated; otherwise it
+ * is split with numpy.array_split chunk sizes.
+ *
+ *  q_lens, kv_lens  host int32 [n_req]: new tokens and total KV rows (new included)
+ *                   per request, in batch order; 0 <= q_len <= kv_len.
+ *  P                PCP size, 1 <= P <= 64.
+ *  T_loc            host out int32 [P]: local rows of each rank.
+ *  n_vrows          host out: virtual rows per rank (equal on every rank: 2 per split
+ *                   request, 1 per replicated request).
+ *  T_glob           host out: sum of q_lens.
+ * Errors: INVALID_ARG for null pointers, n_req < 0, P out of range, q_len > kv_len,
+ * negative lengths, or totals (sum kv_lens, sum of T_loc) that do not fit int32.
+ */
+mla_status pcp_plan_sizes(const int32_t* q_lens, const int32_t* kv_lens, int32_t n_req,
+                          int32_t P, int32_t* T_loc, int32_t* n_vrows, int64_t* T_glob);
+
+/*
+ * pcp_partition — the DualChunkSwap plan on the GPU (integer work, deterministic).
+ * Source: as pcp_plan_sizes; the merge map restores global scheduled-token order
+ * ("DualChunkSwap partitioning", last paragraph).
+ *
+ * Inputs (device int32 [n_req]): q_lens, kv_lens, kv_start (first packed KV row of
+ * each request). Sizes T_glob, n_vrows, T_loc_total (= sum of T_loc) must be the ones
+ * pcp_plan_sizes returned for the same lengths.
+ * Outputs (device int32), ranks concatenated in rank order; rank r's rows start at
+ * row_off[r] = T_loc[0] + ... + T_loc[r-1]:
+ *  cu_seqlens_glob [n_req+1]           global token offsets of the requests.
+ *  cu_seqlens_q    [P][n_vrows+1]      per rank, local token offsets of its virtual
+ *                                      rows (each rank starts at 0).
+ *  vrow_req        [P][n_vrows]        request of each virtual row.
+ *  vrow_kv_start   [P][n_vrows]        kv_start of that request.
+ *  vrow_kv_len     [P][n_vrows]        last position of the virtual row + 1.
+ *  local_gidx      [T_loc_total]       global token of each local row.
+ *  positions       [T_loc_total]       kv_len - q_len + (index of the token among the
+ *                                      request's new tokens).
+ *  slot            [T_loc_total]       kv_start + position (packed KV row).
+ *  merge_src       [T_glob][P]         row (in the rank-concatenated buffers) that rank
+ *                                      p contributes to global token t, else -1. Split
+ *                                      tokens have one entry (their rank); replicated
+ *                                      tokens only rank 0's row.
+ * Rank-local order: requests in batch order; a split request gives chunk r then chunk
+ * 2P-1-r (two virtual rows); a replicated request one virtual row.
+ * Errors: INVALID_ARG for null pointers or sizes out of range; HIP on launch failure.
+ */
+mla_status pcp_partition(const int32_t* q_lens, const int32_t* kv_lens, const int32_t* kv_start,
+                         int32_t n_req, int32_t P, int64_t T_glob, int32_t n_vrows,
+                         int64_t T_loc_total, int32_t* cu_seqlens_glob, int32_t* cu_seqlens_q,
+                         int32_t* vrow_req, int32_t* vrow_kv_start, int32_t* vrow_kv_len,
+                         int32_t* local_gidx, int32_t* positions, int32_t* slot,
+                         int32_t* merge_src, void* stream);
+
+/*
+ * pcp_kv_insert — write a rank's local latent/rope KV rows into the full packed KV at
+ * their slots: the single-GPU stand-in for the latent-KV all-gather that gives every
+ * rank the full KV for cache insertion and attention ("[Core] Add MRV2 virtual-batch
+ * PCP for MLA", "DualChunkSwap partitioning"). A byte copy (bit-exact).
+ *
+ *  local_latent  device [T_loc][D_latent] bf16, or fp8 codes when kv_dtype is FP8.
+ *  local_rope    device [T_loc][D_rope] bf16.
+ *  slot          device int32 [T_loc] destination rows; rows outside [0, N_kv) are
+ *                skipped.
+ *  kv_latent     device [N_kv][D_latent], kv_rope device [N_kv][D_rope] (written).
+ * fp8 tile scales are not touched (they are an input of mla_prefill_partial).
+ * Errors: INVALID_ARG (null, T_loc < 0, N_kv < 0, 16-byte misalignment);
+ * UNSUPPORTED (D_latent not 64/512, D_rope not 16/64, kv_dtype); HIP.
+ */
+mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const int32_t* slot,
+                         int32_t T_loc, int32_t D_latent, int32_t D_rope, int32_t kv_dtype,
+                         int64_t N_kv, void* kv_latent, void* kv_rope, void* stream);
+
+/*
+ * mla_prefill_partial — one rank's partial MLA attention against the full KV, without
+ * the sink. Absorbed MLA: every query head attends one shared latent KV head, key =
+ * latent || rope (D_latent + D_rope), value = latent (D_latent). Each PCP rank computes
+ * a local partial whose LSE/output are merged later with the sink applied once
+ * ("[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid KV and MegaMoE",
+ * "Purpose"); the rank attends the full all-gathered latent KV ("[Core] Add MRV2
+ * virtual-batch PCP for MLA", "DualChunkSwap partitioning").
+ *
+ * For local row i (virtual row v, position p = positions[i]) and head h:
+ *   dense  (topk_idx == NULL): keys are KV rows vrow_kv_start[v] + j, j = 0..p;
+ *   sparse (topk_idx != NULL): keys j in {topk_idx[i][*] in [0, p]} union
+ *          [max(0, p-window+1), p], counted once (entries -1 or outside [0, p] are
+ *          pads; order does not matter).
+ *   S_j = scale * <q[i][h], key_j>; O = softmax(S) @ latent (bf16, round to nearest
+ *   even); LSE = log(sum_j exp(S_j)) (fp32, natural log). No sink.
+ * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]).
+ */
+typedef struct mla_partial_args {
+    const void* q;               /* device bf16 [T_loc][H][D_latent + D_rope]            */
+    const void* latent_kv;       /* device [N_kv][D_latent] bf16, or fp8 codes            */
+    const float* kv_scale;       /* device fp32 [ceil(N_kv/64)] (fp8), else NULL          */
+    const void* rope_k;          /* device bf16 [N_kv][D_rope]                            */
+    const int32_t* cu_seqlens_q; /* device [n_vrows+1] local token offsets (this rank)    */
+    const int32_t* vrow_kv_start;/* device [n_vrows] packed KV offset of the row's request */
+    const int32_t* positions;    /* device [T_loc] causal position of each local token;
+                                    increasing by one inside a virtual row              */
+    const int32_t* topk_idx;     /* device [T_loc][topk] request-relative, or NULL       */
+    int32_t topk;                /* entries per row of topk_idx (<= 2048), 0 when dense   */
+    int32_t window;              /* sliding window added to the sparse set (0 = none)     */
+    int32_t n_vrows;
+    int32_t T_loc;
+    int32_t H;                   /* query heads, 1..128                                    */
+    int32_t D_latent;            /* 512 (or 64)                                            */
+    int32_t D_rope;              /* 64 (or 16)                                             */
+    int32_t kv_dtype;            /* MLA_KV_BF16 or MLA_KV_FP8_E4M3                         */
+    int64_t N_kv;                /* rows of latent_kv / rope_k                             */
+    float scale;                 /* softmax scale                                          */
+    void* o_partial;             /* device bf16 out [T_loc][H][D_latent]                   */
+    float* lse;                  /* device fp32 out [T_loc][H]                             */
+} mla_partial_args;
+
+/* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales);
+ * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, sparse with bf16 KV or
+ * with H not a multiple of 32, dtype); HIP. */
+mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
+
+/*
+ * pcp_lse_merge — merge per-rank partials into global token order with the sink once.
+ * Source: "[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid KV and
+ * MegaMoE", "Purpose" and "Main challenges" (merge LSE/output globally, apply attn_sink
+ * only once, never per rank); order restore from "[Core] Add MRV2 virtual-batch PCP for
+ * MLA", "DualChunkSwap partitioning".
+ * For token t, head h, contributors k (rows merge_src[t][k] >= 0) and sink s_h:
+ *   M = max(s_h, max_k L_k); D = exp(s_h - M) + sum_k exp(L_k - M);
+ *   O = sum_k exp(L_k - M) O_k / D (bf16 RNE); LSE = M + log D (fp32).
+ *
+ *  o_cat     device bf16 [R_total][H][D_v]  partial outputs, ranks concatenated.
+ *  lse_cat   device fp32 [R_total][H]       partial LSEs (natural log, no sink).
+ *  merge_src device int32 [T_glob][P]       row per contributor or -1; rows outside
+ *                                           [0, R_total) are ignored.
+ *  sink      device fp32 [H] or NULL (no sink).
+ *  o_out     device bf16 out [T_glob][H][D_v]; lse_out device fp32 [T_glob][H] or NULL.
+ * A row with no contributor gets O = 0 and LSE = s_h (-inf without a sink).
+ * Errors: INVALID_ARG (null, sizes, P out of 1..64, misalignment); UNSUPPORTED (D_v not
+ * a multiple of 8 in 8..1024); HIP.
+ */
+mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
+                         int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
+                         const float* sink, void* o_out, float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PCP_H */

@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, sizes
+plans like the oracle, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from context_mla_prefill_amd import _lib
+from oracle import partition as op
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_pcp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:mla_status|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert _lib.mla_pcp_abi_version() == _lib.ABI_VERSION
+
+
+@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+def test_plan_sizes_match_oracle(seed, P):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 12))
+    q = rng.integers(0, 70, size=n)
+    kv = q + rng.integers(0, 5, size=n)
+    T_loc, nv, tg = _lib.pcp_plan_sizes(q, kv, P)
+    plan = op.partition(q, kv, np.zeros(n, int), P)
+    assert tg == plan.T_glob
+    assert T_loc == [rp.T_loc for rp in plan.ranks]
+    assert all(nv == rp.n_vrows for rp in plan.ranks)
+
+
+def _status(fn):
+    try:
+        fn()
+    except _lib.MlaError as e:
+        return e.status, str(e)
+    return 0, ""
+
+
+def test_plan_sizes_errors():
+    assert _status(lambda: _lib.pcp_plan_sizes([4], [3], 2))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _status(lambda: _lib.pcp_plan_sizes([4], [4], 0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _status(lambda: _lib.pcp_plan_sizes([4], [4], 65))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert _status(lambda: _lib.pcp_plan_sizes([-1], [4], 2))[0] == _lib.MLA_ERR_INVALID_ARG
+    big = np.full(3, 2 ** 30, dtype=np.int64).astype(np.int32)
+    assert _status(lambda: _lib.pcp_plan_sizes(big, big, 2))[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+def _args(**kw):
+    base = dict(q=None, latent_kv=None, rope_k=None, cu_seqlens_q=None, vrow_kv_start=None, positions=None,
+                n_vrows=1, T_loc=4, H=16, D_latent=512, D_rope=64, scale=1 / 24, o_partial=None, lse=None,
+                N_kv=16)
+    base.update(kw)
+    return _lib.make_partial_args(**base)
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address; never dereferenced on these paths
+
+
+class _P:
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_partial_validation_errors():
+    call = lambda a: _status(lambda: _lib.mla_prefill_partial(a, stream=0))
+    assert call(_args())[0] == _lib.MLA_ERR_INVALID_ARG  # null pointers
+    f = _P(FAKE)
+    ok = dict(q=f, latent_kv=f, rope_k=f, cu_seqlens_q=f, vrow_kv_start=f, positions=f, o_partial=f, lse=f)
+    assert call(_args(**ok, D_latent=128))[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**ok, H=0))[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**ok, H=129))[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**ok, scale=0.0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, scale=float("nan")))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, T_loc=-1))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, n_vrows=0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, kv_dtype=7))[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**{**ok, "q": _P(FAKE + 2)}))[0] == _lib.MLA_ERR_INVALID_ARG  # misaligned
+    assert call(_args(**ok, kv_dtype=_lib.MLA_KV_FP8_E4M3))[0] == _lib.MLA_ERR_UNSUPPORTED  # dense fp8
+    assert call(_args(**ok, topk_idx=f, topk=4096, kv_dtype=1, kv_scale=f, H=64))[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, H=64))[0] == _lib.MLA_ERR_INVALID_ARG  # no scale
+    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=16))[0] == _lib.MLA_ERR_UNSUPPORTED
+    st, msg = call(_args(**ok, D_rope=32))
+    assert st == _lib.MLA_ERR_UNSUPPORTED and "dims" in msg
+    # empty shard: nothing to do, OK without touching any pointer
+    assert call(_args(T_loc=0, n_vrows=0))[0] == 0
+
+
+def test_merge_and_insert_validation_errors():
+    f = _P(FAKE)
+    m = lambda **kw: _status(lambda: _lib.pcp_lse_merge(**{**dict(
+        o_cat=f, lse_cat=f, merge_src=f, P=2, T_glob=4, H=4, D_v=64, R_total=8, sink=None, o_out=f,
+        lse_out=None, stream=0), **kw}))
+    assert m(P=0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert m(D_v=12)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert m(merge_src=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert m(o_out=_P(FAKE + 4))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert m(T_glob=0)[0] == 0
+    ins = lambda **kw: _status(lambda: _lib.pcp_kv_insert(**{**dict(
+        local_latent=f, local_rope=f, slot=f, T_loc=4, D_latent=512, D_rope=64, kv_dtype=0, N_kv=8,
+        kv_latent=f, kv_rope=f, stream=0), **kw}))
+    assert ins(D_latent=100)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert ins(kv_dtype=3)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert ins(slot=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert ins(T_loc=-2)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert ins(T_loc=0)[0] == 0
+
+
+def test_partition_validation_errors():
+    f = _P(FAKE)
+    p = lambda **kw: _status(lambda: _lib.pcp_partition(**{**dict(
+        q_lens=_Len(2, FAKE), kv_lens=f, kv_start=f, P=2, T_glob=10, n_vrows=3, T_loc_total=10,
+        cu_seqlens_glob=f, cu_seqlens_q=f, vrow_req=f, vrow_kv_start=f, vrow_kv_len=f, local_gidx=f,
+        positions=f, slot=f, merge_src=f, stream=0), **kw}))
+    assert p(P=0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert p(n_vrows=5)[0] == _lib.MLA_ERR_INVALID_ARG  # more than 2 per request
+    assert p(n_vrows=1)[0] == _lib.MLA_ERR_INVALID_ARG  # fewer than 1 per request
+    assert p(merge_src=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert p(T_glob=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+
+
+class _Len(_P):
+    def __init__(self, n, addr):
+        super().__init__(addr)
+        self.n = n
+
+    def numel(self):
+        return self.n

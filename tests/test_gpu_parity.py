@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path against the fp64 oracle on the same seeded inputs.
+
+Integer maps (partition, positions, slots, merge map) and the KV insert are bit-exact;
+partial and merged O / LSE meet max|O-O_ref| <= 1e-2 and max|LSE-LSE_ref| <= 1e-3
+(3e-2 on O for the fp8 sparse workload), plus a relative-error sanity bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import helpers as hp
+from context_mla_prefill_amd import _lib, synth
+from context_mla_prefill_amd import pipeline as pp
+from oracle import attention as oa
+from oracle import merge as om
+from oracle import numerics as on
+from oracle import partition as op
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL = 1e-2, 1e-3
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_plan(pl, plan):
+    """Bit-exact comparison of the device plan with the oracle's partition."""
+    torch.cuda.synchronize()
+    assert pl.T_glob == plan.T_glob
+    assert np.array_equal(pl.cu_glob.cpu().numpy(), plan.cu_seqlens_glob)
+    for r, rp in enumerate(plan.ranks):
+        rows = pl.rank_rows(r)
+        assert pl.T_loc[r] == rp.T_loc and pl.row_off[r] == plan.row_off[r]
+        assert np.array_equal(pl.local_gidx[rows].cpu().numpy(), rp.local_gidx)
+        assert np.array_equal(pl.positions[rows].cpu().numpy(), rp.positions)
+        assert np.array_equal(pl.slot[rows].cpu().numpy(), rp.slot)
+        assert np.array_equal(pl.cu_q[r].cpu().numpy(), rp.cu_seqlens_q)
+        assert np.array_equal(pl.vrow_req[r].cpu().numpy(), rp.vrow_req)
+        assert np.array_equal(pl.vrow_kv_start[r].cpu().numpy(), rp.vrow_kv_start)
+        assert np.array_equal(pl.vrow_kv_len[r].cpu().numpy(), rp.vrow_kv_len)
+    assert np.array_equal(pl.merge_src.cpu().numpy(), plan.merge_src)
+
+
+class DenseRun:
+    """Runs partition -> insert -> P partials -> merge for a bf16 dense workload."""
+
+    def __init__(self, w):
+        self.w = w
+        self.plan = hp.oracle_plan(w)
+        print(f"[run] workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
+        self.q_bits = synth.q_rows(w)
+        self.lat_bits = synth.latent_rows(w)
+        self.rope_bits = synth.rope_rows(w)
+        self.sink = synth.sink(w)
+        q = dev_bf16(self.q_bits)
+        lat_full, rope_full = dev_bf16(self.lat_bits), dev_bf16(self.rope_bits)
+        self.pl = pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+        pp.run_partition(pl)
+        # Full KV with every new-token row poisoned (NaN); the inserts must restore it.
+        self.kv_lat, self.kv_rope = lat_full.clone(), rope_full.clone()
+        new_rows = torch.unique(pl.slot.long())
+        self.kv_lat.view(torch.int16)[new_rows] = 0x7FC0
+        self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl)
+        self.sink_d = torch.from_numpy(self.sink).cuda()
+        for r in range(w.P):
+            ri = pp.rank_inputs(pl, r, q, lat_full, rope_full)
+            _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
+                               _lib.MLA_KV_BF16, w.N_kv, self.kv_lat, self.kv_rope)
+            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale)
+            _lib.mla_prefill_partial(args)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl)
+        torch.cuda.synchronize()
+        self.lat_full, self.rope_full = lat_full, rope_full
+
+    def check_insert(self):
+        assert torch.equal(self.kv_lat.view(torch.int16), self.lat_full.view(torch.int16))
+        assert torch.equal(self.kv_rope.view(torch.int16), self.rope_full.view(torch.int16))
+
+    def check_values(self, tokens):
+        w, plan = self.w, self.plan
+        ref = hp.oracle_dense(w, plan, self.q_bits, self.lat_bits, self.rope_bits, self.sink, tokens)
+        o_cat = on.bf16_to_f64(host_bits(self.bufs.o_cat))
+        lse_cat = self.bufs.lse_cat.cpu().numpy()
+        tokset = set(int(t) for t in tokens)
+        for r, rp in enumerate(plan.ranks):
+            rows = [i for i, g in enumerate(rp.local_gidx) if int(g) in tokset]
+            if not rows:
+                continue
+            gi = [int(rp.local_gidx[i]) for i in rows]
+            cat = plan.row_off[r] + np.asarray(rows)
+            hp.compare(f"workload {w.cfg} rank {r} partial", o_cat[cat], lse_cat[cat],
+                       np.stack([ref[g][0] for g in gi]), np.stack([ref[g][1] for g in gi]), O_TOL, LSE_TOL)
+        toks = np.asarray(sorted(tokset))
+        o = on.bf16_to_f64(host_bits(self.bufs.o))[toks]
+        lse = self.bufs.lse.cpu().numpy()[toks]
+        hp.compare(f"workload {w.cfg} merged", o, lse, np.stack([ref[g][2] for g in toks]),
+                   np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
+        return ref
+
+
+@pytest.fixture(scope="module")
+def tiny(gpu_lib):
+    return DenseRun(synth.workload(1))
+
+
+def test_tiny_plan(tiny):
+    check_plan(tiny.pl, tiny.plan)
+
+
+def test_tiny_insert(tiny):
+    tiny.check_insert()
+
+
+def test_tiny_values(tiny):
+    tiny.check_values(np.arange(tiny.w.T_glob))
+
+
+def test_tiny_sink_once_negative(tiny):
+    """Partials with the sink already applied per rank, merged with the sink again,
+    must miss the oracle: the test is sensitive to a doubled sink."""
+    w = tiny.w
+    o = tiny.bufs.o_cat.float()
+    lse = tiny.bufs.lse_cat.clone()
+    s = tiny.sink_d[None, :]
+    o_bad = (o * torch.sigmoid(lse - s)[..., None]).to(torch.bfloat16)
+    lse_bad = torch.logaddexp(lse, s)
+    out = torch.empty_like(tiny.bufs.o)
+    _lib.pcp_lse_merge(o_bad, lse_bad, tiny.pl.merge_src, w.P, w.T_glob, w.H, w.Dl, tiny.pl.T_total,
+                       tiny.sink_d, out, None)
+    torch.cuda.synchronize()
+    ref = hp.oracle_dense(w, tiny.plan, tiny.q_bits, tiny.lat_bits, tiny.rope_bits, tiny.sink,
+                          np.arange(w.T_glob))
+    got = on.bf16_to_f64(host_bits(out))
+    want = np.stack([ref[t][2] for t in range(w.T_glob)])
+    assert np.max(np.abs(got - want)) > 3 * O_TOL
+
+
+@pytest.fixture(scope="module")
+def dense8k(gpu_lib):
+    return DenseRun(synth.workload(2))
+
+
+def test_dense8k_plan(dense8k):
+    check_plan(dense8k.pl, dense8k.plan)
+
+
+def test_dense8k_insert(dense8k):
+    dense8k.check_insert()
+
+
+def test_dense8k_values_full(dense8k):
+    dense8k.check_values(np.arange(dense8k.w.T_glob))
+
+
+EDGE = [
+    # (seed, q_lens, kv_lens, P, H, Dl, Dr)
+    (101, [1000], [1000], 3, 16, 512, 64),  # ragged chunks and tiles
+    (102, [37, 3, 1, 1, 200, 9], [37, 3, 50, 7, 260, 9], 2, 16, 512, 64),  # short prefill, decodes, continuation
+    (103, [77], [77], 1, 16, 512, 64),  # P = 1 is the identity
+    (104, [130, 5, 1], [130, 5, 300], 4, 4, 64, 16),  # tiny dims, replicated rows
+    (105, [64, 64], [64, 64], 2, 2, 64, 16),  # two requests, H = 2
+    (106, [600, 1], [700, 900], 2, 64, 512, 64),  # H = 64
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[str(c[0]) for c in EDGE])
+def test_edge_cases(gpu_lib, case):
+    seed, q, kv, P, H, Dl, Dr = case
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=Dl, Dr=Dr)
+    run = DenseRun(w)
+    check_plan(run.pl, run.plan)
+    run.check_insert()
+    run.check_values(np.arange(w.T_glob))
+
+
+def test_empty_batch(gpu_lib):
+    pl = pp.alloc_plan(np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), 2)
+    pp.run_partition(pl)
+    torch.cuda.synchronize()
+    assert pl.T_glob == 0 and pl.cu_glob.cpu().tolist() == [0]
+
+
+def test_replicas_merged_once_negative(gpu_lib):
+    """Merging every replica of a replicated row (instead of rank 0's only) must fail."""
+    w = synth.custom(107, [3, 1, 16], [3, 40, 16], P=4, H=16, Dl=512, Dr=64)
+    run = DenseRun(w)
+    run.check_values(np.arange(w.T_glob))
+    src = run.pl.merge_src.clone()
+    plan = run.plan
+    for r, rp in enumerate(plan.ranks):
+        for i, g in enumerate(rp.local_gidx):
+            if w.q_lens[int(np.searchsorted(plan.cu_seqlens_glob, g, side="right") - 1)] < 2 * w.P:
+                src[int(g), r] = plan.row_off[r] + i
+    out = torch.empty_like(run.bufs.o)
+    _lib.pcp_lse_merge(run.bufs.o_cat, run.bufs.lse_cat, src, w.P, w.T_glob, w.H, w.Dl, run.pl.T_total,
+                       run.sink_d, out, None)
+    torch.cuda.synchronize()
+    ref = hp.oracle_dense(w, plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, np.arange(w.T_glob))
+    got = on.bf16_to_f64(host_bits(out))
+    want = np.stack([ref[t][2] for t in range(w.T_glob)])
+    assert np.max(np.abs(got - want)) > O_TOL
+
+
+@pytest.mark.parametrize("T,P", [(64, 2), (96, 4), (45, 3)])
+def test_merge_of_oracle_key_split_partials(gpu_lib, T, P):
+    """The general <=P-contributor merge, fed with oracle-made partials of a DualChunkSwap
+    key split (each rank attends only its own chunks' keys)."""
+    rng = np.random.default_rng(T * 10 + P)
+    H, Dl, Dr = 4, 64, 16
+    q = rng.standard_normal((T, H, Dl + Dr)) * 0.5
+    lat = rng.standard_normal((T, Dl)) * 0.5
+    rope = rng.standard_normal((T, Dr)) * 0.5
+    sink = rng.standard_normal(H).astype(np.float32)
+    plan = op.partition([T], [T], [0], P)
+    o_cat = np.zeros((T * P, H, Dl))
+    lse_cat = np.full((T * P, H), -np.inf)
+    src = np.full((T, P), -1, np.int32)
+    for t in range(T):
+        for r in range(P):
+            keys = plan.ranks[r].positions
+            keys = keys[keys <= t]
+            if len(keys) == 0:
+                continue
+            o0, l0, _, _ = oa.attend_keyset(q[t], lat[keys], rope[keys], 0.3)
+            o_cat[t * P + r], lse_cat[t * P + r] = o0, l0
+            src[t, r] = t * P + r
+    o_bits = synth.bf16_bits(o_cat.astype(np.float32))
+    lse32 = lse_cat.astype(np.float32)
+    o_out = torch.empty(T, H, Dl, dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    _lib.pcp_lse_merge(dev_bf16(o_bits), torch.from_numpy(lse32).cuda(), torch.from_numpy(src).cuda(), P, T,
+                       H, Dl, T * P, torch.from_numpy(sink).cuda(), o_out, lse_out)
+    torch.cuda.synchronize()
+    # oracle merge of the same stored partials
+    want_o, want_l = om.merge(on.bf16_to_f64(o_bits), lse32.astype(np.float64), src, sink.astype(np.float64))
+    got_o = on.bf16_to_f64(host_bits(o_out))
+    np.testing.assert_allclose(got_o, want_o, atol=4e-3, rtol=1e-2)
+    np.testing.assert_allclose(lse_out.cpu().numpy(), want_l, atol=1e-5, rtol=1e-6)
+    # and it equals unsharded attention with the sink once
+    for t in range(T):
+        _, _, o, l = oa.attend_keyset(q[t], lat[:t + 1], rope[:t + 1], 0.3, sink.astype(np.float64))
+        assert np.max(np.abs(got_o[t] - o)) < O_TOL and np.max(np.abs(lse_out[t].cpu().numpy() - l)) < LSE_TOL

@@ -69,10 +69,12 @@ class DenseRun:
         self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
         self.bufs = pp.alloc_step(pl, w.H, w.Dl)
         self.sink_d = torch.from_numpy(self.sink).cuda()
-        for r in range(w.P):
-            ri = pp.rank_inputs(pl, r, q, lat_full, rope_full)
+        ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full) for r in range(w.P)]
+        # every rank's rows reach the full KV (the all-gather) before any rank attends
+        for r, ri in enumerate(ranks):
             _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
                                _lib.MLA_KV_BF16, w.N_kv, self.kv_lat, self.kv_rope)
+        for r, ri in enumerate(ranks):
             args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl)

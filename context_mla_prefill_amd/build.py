@@ -20,6 +20,10 @@ LIB = os.path.join(PKG, "libmla_pcp.so")
 
 SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense.hip"]
 
+# Per-file flags. The attention kernel keeps O and the scores in VGPRs (MFMA VGPR form)
+# so its rare rescale is plain VALU work, leaving the AGPRs to Q.
+EXTRA = {"attn_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -49,7 +53,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         _run(cmd)

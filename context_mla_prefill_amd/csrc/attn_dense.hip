@@ -8,19 +8,26 @@
 // context-parallel prefill for hybrid KV and MegaMoE", "Purpose").
 //
 // Work decomposition
-//  * A workgroup (4 waves) owns BM = 128 rows of one virtual row, where a row is a
+//  * A workgroup (4 waves) owns BM = 64 rows of one virtual row, where a row is a
 //    (token, head) pair: all heads share the KV, so token x head is the M dimension.
-//    Each wave owns 32 rows; its Q rows live in registers for the whole KV loop.
-//  * KV tiles of BN keys are staged HBM -> LDS once per workgroup and shared by all
-//    heads and waves.
+//    The waves form two pairs; a pair owns 32 rows and both of its waves keep the full
+//    Q of those rows in registers for the whole KV loop.
+//  * KV tiles of BN = 64 keys move HBM -> LDS with direct-to-LDS loads into a double
+//    buffer (the next tile streams in while the current one is used) and are shared by
+//    all heads and waves. 16-byte chunks are XOR-swizzled by row to spread LDS banks.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, A = K from
-//    LDS, B = Q^T from registers), so each lane holds scores of ONE query row: the
-//    online-softmax max needs one cross-half exchange and the running sum stays
-//    per-lane until the epilogue.
-//  * The output is accumulated transposed, O^T += V^T P^T, so the P fragment is the
-//    score accumulator re-packed to bf16 in place (no LDS round trip) and the per-row
-//    rescale is a per-lane scalar. The key order inside a 16-key MFMA block is the
-//    one the score layout gives each lane; V^T is read in that same order.
+//    LDS, B = Q^T from registers); wave s of a pair scores keys [32 s, 32 s + 32) of the
+//    tile. Each lane then holds scores of ONE query row, so the row max needs one
+//    cross-half exchange and the running sum stays per lane until the epilogue.
+//  * The output is accumulated transposed, O^T += V^T P^T; wave s of a pair owns output
+//    columns [256 s, 256 s + 256) and needs P for all 64 keys, so the two waves swap
+//    their bf16 P fragments through LDS. The P fragment is the score accumulator
+//    re-packed in place; V^T comes from transposing LDS reads (ds_read_b64_tr_b16) in
+//    the key order the score layout gives each lane.
+//  * Online softmax with a lazy reference max: the reference of a row moves only when a
+//    tile max exceeds it by more than kRescale (log2 units). Tiles that move no
+//    reference (nearly all of them) need no max exchange and no O rescale; a tile that
+//    does takes a workgroup-uniform slow path with one extra barrier.
 //  * Workgroups are launched longest-first (reverse of the flattened tile order), so
 //    the long late-chunk tiles start first and the short ones fill the tail.
 #include <math.h>
@@ -33,9 +40,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 64;   // rows per workgroup: two wave pairs of 32 rows
-constexpr int BN = 32;   // keys per KV tile
+constexpr int BN = 64;   // keys per KV tile (32 per wave of a pair)
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -46,10 +54,21 @@ struct Shape {
     static constexpr int DQK = DL + DR;
     static constexpr int KB = DQK / 16;      // 16-wide k-blocks of Q K^T
     static constexpr int NB = DL / 32;       // 32-wide column blocks of O
-    static constexpr int STRIDE = DQK + 8;   // LDS row stride (bf16): +16 B breaks bank aliasing
-    static constexpr int VECS = DQK / 8;     // 16-byte vectors per key row
-    static constexpr int LAT_VECS = DL / 8;
-    static constexpr int ROPE_VECS = DR / 8;
+    static constexpr int LAT_VECS = DL / 8;      // 16-byte chunks of a latent row
+    static constexpr int ROPE_VECS = DR / 8;     // 16-byte chunks of a rope row
+    // LDS tile: latent rows at a stride of DL*2 + 16 bytes (one direct-to-LDS load per
+    // row when DL*2 == 1024, several rows per load otherwise), then rope rows at a
+    // stride of DR*2 + 16 bytes. The 16-byte pad puts consecutive rows on different
+    // banks for both the row reads of Q K^T and the transposing reads of P V.
+    static constexpr int LAT_STRIDE = DL * 2 + 16;
+    static constexpr int ROPE_STRIDE = DR * 2 + 16;
+    static constexpr int ROPE_OFF = BN * LAT_STRIDE;
+    static constexpr int TILE_BYTES = ROPE_OFF + BN * ROPE_STRIDE;
+    // rows written per wave-wide load (a load covers 64 lanes x 16 bytes)
+    static constexpr int LAT_ROWS_PER_LOAD = 64 / (LAT_VECS + 1) > 0 ? 64 / (LAT_VECS + 1) : 1;
+    static constexpr int ROPE_ROWS_PER_LOAD = 64 / (ROPE_VECS + 1);
+    static constexpr int LAT_LOADS = DL * 2 == 1024 ? BN : (BN + LAT_ROWS_PER_LOAD - 1) / LAT_ROWS_PER_LOAD;
+    static constexpr int ROPE_LOADS = (BN + ROPE_ROWS_PER_LOAD - 1) / ROPE_ROWS_PER_LOAD;
     static_assert(DQK % 16 == 0 && DL % 32 == 0 && DR % 8 == 0, "tile shape");
 };
 
@@ -102,15 +121,69 @@ __device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ 
     tile_out = s_tile;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// One wave-wide direct-to-LDS load: lane l copies 16 bytes from `src` to LDS address
+// lds_base + 16*l.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Issues the direct-to-LDS loads of KV tile kt (keys [kt*BN, kt*BN+BN) of the request)
+// into `dst`. A load writes 64 consecutive 16-byte LDS chunks, one per lane; lanes that
+// would land on a row pad are switched off. Keys past the tile's extent repeat the last
+// valid row (finite values; their scores are masked). Wave w issues loads w, w+4, ...
+template <class S, int DL, int DR>
+__device__ __forceinline__ void load_tile(char* dst, const char* __restrict__ lat, const char* __restrict__ rope,
+                                          int64_t kv0, int kt, int kv_hi, int64_t N_kv, int wave, int lane) {
+    constexpr int LV = S::LAT_VECS + 1, RV = S::ROPE_VECS + 1;
+    const int64_t last = min((int64_t)kv_hi - 1, N_kv - 1 - kv0);
+    // latent: row k of the load is lanes [k*LV, k*LV + LAT_VECS)
+    {
+        const int k = DL * 2 == 1024 ? 0 : lane / LV;
+        const int c = DL * 2 == 1024 ? lane : lane - k * LV;
+        const bool on = DL * 2 == 1024 || (c < S::LAT_VECS && k < S::LAT_ROWS_PER_LOAD);
+#pragma unroll
+        for (int i = 0; i < (S::LAT_LOADS + 3) / 4; ++i) {
+            const int n = i * 4 + wave;
+            if (n >= S::LAT_LOADS) break;  // wave-uniform
+            const int r = n * S::LAT_ROWS_PER_LOAD + k;
+            const int64_t j = min((int64_t)kt * BN + r, last);
+            if (DL * 2 == 1024 || (on && r < BN))
+                lds_dma16(lat + (kv0 + j) * (DL * 2) + c * 16, dst + n * S::LAT_ROWS_PER_LOAD * S::LAT_STRIDE);
+        }
+    }
+    // rope: ROPE_ROWS_PER_LOAD rows per load
+    {
+        const int k = lane / RV;
+        const int c = lane - k * RV;
+        const bool on = c < S::ROPE_VECS && k < S::ROPE_ROWS_PER_LOAD;
+#pragma unroll
+        for (int i = 0; i < (S::ROPE_LOADS + 3) / 4; ++i) {
+            const int n = i * 4 + ((wave + 2) & 3);  // start on the waves with fewer latent loads
+            if (n >= S::ROPE_LOADS) break;
+            const int r = n * S::ROPE_ROWS_PER_LOAD + k;
+            const int64_t j = min((int64_t)kt * BN + r, last);
+            if (on && r < BN)
+                lds_dma16(rope + (kv0 + j) * (DR * 2) + c * 16,
+                          dst + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
+        }
+    }
+}
+
 template <int DL, int DR>
 __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
-    const __bf16* __restrict__ q, const uint4* __restrict__ lat, const uint4* __restrict__ rope,
+    const __bf16* __restrict__ q, const char* __restrict__ lat, const char* __restrict__ rope,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
     using S = Shape<DL, DR>;
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * S::STRIDE];
-    __shared__ __attribute__((aligned(16))) float4 Sx[NT / 64][4][64];  // partial-score exchange
+    __shared__ __attribute__((aligned(1024))) char kv_lds0[S::TILE_BYTES];  // KV tile double buffer:
+    __shared__ __attribute__((aligned(1024))) char kv_lds1[S::TILE_BYTES];  // two separate objects
+    __shared__ __attribute__((aligned(16))) uint4 Px[NT / 64][2][64];  // P fragment exchange
+    __shared__ float mx[NT / 64][64];                                  // tile-max exchange (slow path)
+    __shared__ int flag[NT / 64];
     __shared__ int sh[NT];
     __shared__ int s_maxpos[NT / 64];
 
@@ -121,7 +194,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int pair = wave >> 1;
-    const int side = wave & 1;    // which half of the QK k-blocks and of the O columns
+    const int side = wave & 1;    // keys [32 side, +32) of each tile; O columns [DL/2 side, +DL/2)
     const int lane = tid & 63;
     const int half = lane >> 5;   // which 8-element half of a 16-wide k-block this lane holds
     const int l32 = lane & 31;
@@ -140,20 +213,13 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     for (int off = 32; off >= 1; off >>= 1) mp = max(mp, __shfl_xor(mp, off));
     if (lane == 0) s_maxpos[wave] = mp;
 
-    // Q^T fragments of this wave's k-blocks: lane holds row l32, elements
-    // [16 kb + 8 half, +8) of each block.
-    constexpr int KB0 = (S::KB + 1) / 2;  // k-blocks of side 0; side 1 takes the rest
-    constexpr int NB0 = S::NB / 2;        // O column blocks per side
-    const int kb_lo = side ? KB0 : 0;
-    const int kb_n = side ? S::KB - KB0 : KB0;
-    bf16x8 qf[KB0];
+    // Q^T fragments: lane holds row l32, elements [16 kb + 8 half, +8) of every k-block.
+    bf16x8 qf[S::KB];
     {
         const __bf16* qrow = q + grow * S::DQK + 8 * half;
 #pragma unroll
-        for (int k = 0; k < KB0; ++k) {
-            qf[k] = (valid && k < kb_n) ? *reinterpret_cast<const bf16x8*>(qrow + (kb_lo + k) * 16)
-                                        : bf16x8{};
-        }
+        for (int kb = 0; kb < S::KB; ++kb)
+            qf[kb] = valid ? *reinterpret_cast<const bf16x8*>(qrow + kb * 16) : bf16x8{};
     }
     __syncthreads();
     int kv_hi = s_maxpos[0];
@@ -161,109 +227,133 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     for (int w = 1; w < NT / 64; ++w) kv_hi = max(kv_hi, s_maxpos[w]);
     kv_hi += 1;
 
+    constexpr int NB0 = S::NB / 2;  // O column blocks per wave
     f32x16 acc_o[NB0];
 #pragma unroll
     for (int d = 0; d < NB0; ++d) acc_o[d] = f32x16{};
-    float m_run = -INFINITY;  // running (lazy) max of log2-domain scores of this lane's row
-    float l_run = 0.0f;       // running sum over this lane's half of the keys
+    float m_ref = -INFINITY;  // lazy reference max (log2 domain) of this lane's row
+    float l_run = 0.0f;       // running sum over this lane's share of the keys
+
+    // Per-lane LDS offsets inside a tile (everything else is an immediate):
+    //  * Q K^T reads: key row 32*side + l32, 8 elements at 8*half of each 16-wide k-block;
+    //  * V^T reads: key row 4*half + (lane%16)/4 (+16 kb, +8), dims 16*((lane/16)%2) + 4*(lane%4).
+    const int k_lat_off = (32 * side + l32) * S::LAT_STRIDE + 16 * half;
+    const int k_rope_off = S::ROPE_OFF + (32 * side + l32) * S::ROPE_STRIDE + 16 * half;
+    const int v_off = (4 * half + ((lane & 15) >> 2)) * S::LAT_STRIDE +
+                      2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     const int n_tiles = (kv_hi + BN - 1) / BN;
-    for (int kt = 0; kt < n_tiles; ++kt) {
-        __syncthreads();
-        // Stage KV rows [kt*BN, kt*BN + BN) of this request: latent || rope, zero past the end.
-        for (int c = tid; c < BN * S::VECS; c += NT) {
-            const int key = c / S::VECS;
-            const int vec = c - key * S::VECS;
-            const int64_t j = (int64_t)kt * BN + key;
-            uint4 val = {0u, 0u, 0u, 0u};
-            if (j < kv_hi && kv0 + j < N_kv) {
-                val = vec < S::LAT_VECS ? lat[(kv0 + j) * S::LAT_VECS + vec]
-                                        : rope[(kv0 + j) * S::ROPE_VECS + (vec - S::LAT_VECS)];
-            }
-            *reinterpret_cast<uint4*>(&Ks[key * S::STRIDE + vec * 8]) = val;
-        }
-        __syncthreads();
 
-        // Partial S^T[key, row] over this wave's k-blocks, keys 8*(i/4) + 4*half + i%4.
+    // One KV tile: wait for it, publish it, start streaming the next tile into the other
+    // buffer, then scores, softmax, P exchange and P V on this one. The two buffers are
+    // distinct LDS objects, so the compiler can tell that the streaming loads never
+    // touch the tile being read and does not wait for them.
+    auto tile_step = [&](const char* kvt, char* nxt, int kt) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
+        __syncthreads();                     // ... and every wave's; the other buffer is free
+        if (kt + 1 < n_tiles) load_tile<S, DL, DR>(nxt, lat, rope, kv0, kt + 1, kv_hi, N_kv, wave, lane);
+        // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
         f32x16 s = f32x16{};
         {
-            const __bf16* kp = &Ks[l32 * S::STRIDE + 8 * half + kb_lo * 16];
+            const char* kl = kvt + k_lat_off;
+            const char* kr = kvt + k_rope_off;
 #pragma unroll
-            for (int k = 0; k < KB0; ++k) {
-                if (k < kb_n) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + k * 16);
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k], s, 0, 0, 0);
-                }
+            for (int kb = 0; kb < S::KB; ++kb) {
+                const char* ap = kb < DL / 16 ? kl + kb * 32 : kr + (kb - DL / 16) * 32;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
             }
         }
-        // Exchange partial scores with the other wave of the pair; both then hold the
-        // same full scores (a + b == b + a exactly) and run the same softmax.
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Sx[wave][c][lane] = make_float4(s[4 * c], s[4 * c + 1], s[4 * c + 2], s[4 * c + 3]);
-        __syncthreads();
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float4 o = Sx[wave ^ 1][c][lane];
-            s[4 * c] += o.x;
-            s[4 * c + 1] += o.y;
-            s[4 * c + 2] += o.z;
-            s[4 * c + 3] += o.w;
-        }
-
         float mloc = -INFINITY;
+        const int key0 = kt * BN + 32 * side + 4 * half;  // key of s[0]
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int j = kt * BN + 8 * (i >> 2) + 4 * half + (i & 3);
+            const int j = key0 + 8 * (i >> 2) + (i & 3);
             const float x = j <= pos ? s[i] * scale_log2 : -INFINITY;
             s[i] = x;
             mloc = fmaxf(mloc, x);
         }
-        // Lazy rescale: the reference max only moves when the tile max exceeds it by more
-        // than kRescale (log2 units), so p <= 2^kRescale and the O rescale is rare.
-        // Numerator and denominator share the reference, so the result is unchanged.
-        const float m_tile = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const bool bump = m_tile > m_run + kRescale;  // also true on the first live tile
-        const float m_new = bump ? m_tile : m_run;
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;
-        float lsum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[i] - m_use);
-            s[i] = p;
-            lsum += p;
-        }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-        if (__ballot(bump)) {
-#pragma unroll
-            for (int d = 0; d < NB0; ++d) acc_o[d] *= alpha;
-        }
-
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));  // max over this wave's 32 keys
+        // Fast path: P against the current reference, published with a "needs a new
+        // reference" flag; the slow path (any wave flagged) agrees on the pair max first.
+        const bool need = mloc > m_ref + kRescale;
+        float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
         bf16x8 pk[2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            pk[0][j] = (__bf16)s[j];
-            pk[1][j] = (__bf16)s[8 + j];
+            pk[0][j] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_use);
+            pk[1][j] = (__bf16)__builtin_amdgcn_exp2f(s[8 + j] - m_use);
         }
-        // O^T[dim, row] += V^T[dim, key] P^T[key, row] over this wave's column blocks;
-        // element j of the lane's k-slice is key 16*kb2 + 8*(j/4) + 4*half + j%4, the
-        // order the score layout produced.
+        Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
+        Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
+        mx[wave][lane] = mloc;
+        const bool any_need = __ballot(need) != 0;
+        if (lane == 0) flag[wave] = any_need;
+        __syncthreads();
+        int slow = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) slow |= flag[w];
+        if (slow) {  // workgroup-uniform
+            const float m_pair = fmaxf(mloc, mx[wave ^ 1][lane]);
+            const bool bump = m_pair > m_ref + kRescale;
+            const float m_new = bump ? m_pair : m_ref;
+            m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_use) : 1.0f;
+            l_run *= alpha;
+            m_ref = m_new;
+#pragma unroll
+            for (int d = 0; d < NB0; ++d) acc_o[d] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pk[0][j] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_use);
+                pk[1][j] = (__bf16)__builtin_amdgcn_exp2f(s[8 + j] - m_use);
+            }
+            __syncthreads();  // everyone has read the flags and the fast-path P
+            Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
+            Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
+            __syncthreads();
+        }
+        float lsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum += __builtin_amdgcn_exp2f(s[i] - m_use);
+        l_run += lsum;
+        // P^T fragments: our two key blocks (tile rows 32*side + [0,32)) and the partner's
+        // (rows 32*(1-side) + [0,32)); the matching V rows are picked by address.
+        const bf16x8 po0 = __builtin_bit_cast(bf16x8, Px[wave ^ 1][0][lane]);
+        const bf16x8 po1 = __builtin_bit_cast(bf16x8, Px[wave ^ 1][1][lane]);
+
+        // O^T[dim, row] += V^T[dim, key] P^T[key, row] over this wave's column blocks.
+        // Element j of the lane's k-slice of a 16-key block is key
+        // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
+        const char* v_own = kvt + v_off + (32 * side) * S::LAT_STRIDE;
+        const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * S::LAT_STRIDE;
 #pragma unroll
         for (int d = 0; d < NB0; ++d) {
-            const int db = side * NB0 + d;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                bf16x8 a;
-                const __bf16* vp = &Ks[(16 * kb2 + 4 * half) * S::STRIDE + db * 32 + l32];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) a[j] = vp[(8 * (j >> 2) + (j & 3)) * S::STRIDE];
-                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb2], acc_o[d], 0, 0, 0);
+            for (int kb = 0; kb < 4; ++kb) {
+                const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * S::LAT_STRIDE + (side * NB0 + d) * 64;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::LAT_STRIDE));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
+                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);
             }
         }
+    };
+
+    load_tile<S, DL, DR>(kv_lds0, lat, rope, kv0, 0, kv_hi, N_kv, wave, lane);
+    for (int kt = 0; kt < n_tiles; kt += 2) {
+        tile_step(kv_lds0, kv_lds1, kt);
+        if (kt + 1 >= n_tiles) break;
+        tile_step(kv_lds1, kv_lds0, kt + 1);
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // Row sums: this lane's share + the other half-wave's + the partner wave's.
+    float l_w = l_run + __shfl_xor(l_run, 32);
+    __syncthreads();
+    mx[wave][lane] = l_w;
+    __syncthreads();
+    const float l_tot = l_w + mx[wave ^ 1][lane];
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (valid) {
         __bf16* orow = o_out + grow * DL;
@@ -278,7 +368,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
                 *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * half) = y;
             }
         }
-        if (side == 0 && half == 0) lse_out[grow] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (side == 0 && half == 0) lse_out[grow] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -286,7 +376,7 @@ template <int DL, int DR>
 hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
     const int64_t grid = ((int64_t)a.T_loc * a.H + BM - 1) / BM + a.n_vrows;
     hipLaunchKernelGGL((dense_partial_kernel<DL, DR>), dim3((unsigned)grid), dim3(NT), 0, stream,
-                       (const __bf16*)a.q, (const uint4*)a.latent_kv, (const uint4*)a.rope_k, a.cu_seqlens_q,
+                       (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.n_vrows, a.H, a.N_kv, a.scale * kLog2e,
                        (__bf16*)a.o_partial, a.lse);
     return hipGetLastError();

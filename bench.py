@@ -189,7 +189,7 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, 64, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, 2048, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -172,6 +172,7 @@ mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t*
         return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: sizes out of range (P=%d H=%d)", P, H);
     if (D_v < 8 || D_v > 1024 || D_v % 8 != 0)
         return fail(MLA_ERR_UNSUPPORTED, "pcp_lse_merge: D_v=%d must be a multiple of 8 in 8..1024", D_v);
+    if (H > 128) return fail(MLA_ERR_UNSUPPORTED, "pcp_lse_merge: H=%d above 128", H);
     if (T_glob == 0) return MLA_OK;
     if (!merge_src || !o_out || (R_total > 0 && (!o_cat || !lse_cat)))
         return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: null pointer");

@@ -10,9 +10,11 @@
 // Per (token t, head h): M = max(s_h, max_k L_k), D = exp(s_h-M) + sum_k exp(L_k-M),
 // O = sum_k exp(L_k-M) O_k / D, LSE = M + log D, all in fp32; O stored bf16 (RNE).
 //
-// HBM-bound streaming: D_v/8 consecutive threads own one (t, h) row and each moves 16
-// bytes per contributor, so every contributor row is read with full-width coalesced
-// loads and the output row written the same way.
+// HBM-bound streaming: one workgroup per token. Its first threads turn the token's
+// contributor LSEs and the sinks into per-(contributor, head) weights in LDS; then the
+// whole workgroup streams the token's H*D_v output elements, 16 bytes per thread and
+// several vectors in flight, reading each contributor's rows (contiguous H*D_v bf16)
+// with full-width coalesced non-temporal loads (every byte is read exactly once).
 #include <math.h>
 
 #include "internal.h"
@@ -21,45 +23,88 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void merge_kernel(
-    const uint4* __restrict__ o_cat, const float* __restrict__ lse_cat,
-    const int32_t* __restrict__ merge_src, int P, int64_t n_rows, int H, int G, int64_t R_total,
-    const float* __restrict__ sink, uint4* __restrict__ o_out, float* __restrict__ lse_out) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t row = gid / G;
-    if (row >= n_rows) return;
-    const int v = (int)(gid - row * G);
-    const int64_t t = row / H;
-    const int h = (int)(row - t * H);
-    const float sig = sink ? sink[h] : -INFINITY;
-    const int32_t* src = merge_src + t * P;
-    float M = sig;
-    for (int k = 0; k < P; ++k) {
-        const int64_t r = src[k];
-        if (r >= 0 && r < R_total) M = fmaxf(M, lse_cat[r * H + h]);
-    }
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float D = 0.0f;
-    if (M != -INFINITY) {
-        D = (sig == -INFINITY) ? 0.0f : expf(sig - M);
+constexpr int NT = 256;
+constexpr int MAXP = 64;
+constexpr int MAXH = 128;
+constexpr int UNROLL = 4;  // vectors per thread in flight
+
+__global__ __launch_bounds__(NT) void merge_kernel(
+    const u32x4* __restrict__ o_cat, const float* __restrict__ lse_cat,
+    const int32_t* __restrict__ merge_src, int P, int H, int G, int64_t R_total,
+    const float* __restrict__ sink, u32x4* __restrict__ o_out, float* __restrict__ lse_out) {
+    __shared__ int rows[MAXP];
+    __shared__ int n_rows;
+    __shared__ float wts[MAXP][MAXH];  // exp(L_k - M) / D per contributor and head
+    const int64_t t = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        int n = 0;
         for (int k = 0; k < P; ++k) {
-            const int64_t r = src[k];
-            if (r < 0 || r >= R_total) continue;
-            const float w = expf(lse_cat[r * H + h] - M);
-            D += w;
-            const uint4 raw = o_cat[(r * H + h) * G + v];
-            const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+            const int64_t r = merge_src[t * P + k];
+            if (r >= 0 && r < R_total) rows[n++] = (int)r;
+        }
+        n_rows = n;
+    }
+    __syncthreads();
+    const int n = n_rows;
+    for (int h = tid; h < H; h += NT) {
+        const float sig = sink ? sink[h] : -INFINITY;
+        float M = sig;
+        for (int k = 0; k < n; ++k) M = fmaxf(M, lse_cat[(int64_t)rows[k] * H + h]);
+        float D = 0.0f;
+        for (int k = 0; k < n; ++k) wts[k][h] = 0.0f;
+        if (M != -INFINITY) {
+            D = sig == -INFINITY ? 0.0f : expf(sig - M);
+            for (int k = 0; k < n; ++k) {
+                const float w = expf(lse_cat[(int64_t)rows[k] * H + h] - M);
+                wts[k][h] = w;
+                D += w;
+            }
+        }
+        const float inv = D > 0.0f ? 1.0f / D : 0.0f;
+        for (int k = 0; k < n; ++k) wts[k][h] *= inv;
+        if (lse_out) lse_out[t * H + h] = M == -INFINITY ? -INFINITY : M + logf(D);
+    }
+    __syncthreads();
+    const int V = H * G;  // 16-byte vectors of this token's output
+    const u32x4* src_base = o_cat;
+    u32x4* dst = o_out + t * V;
+    for (int v0 = tid; v0 < V; v0 += NT * UNROLL) {
+        float acc[UNROLL][8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += w * (float)x[j];
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[u][j] = 0.0f;
+        for (int k = 0; k < n; ++k) {
+            const u32x4* src = src_base + (int64_t)rows[k] * V;
+            u32x4 raw[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int v = v0 + u * NT;
+                raw[u] = v < V ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int v = v0 + u * NT;
+                const float w = v < V ? wts[k][v / G] : 0.0f;
+                const bf16x8 x = __builtin_bit_cast(bf16x8, raw[u]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[u][j] += w * (float)x[j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int v = v0 + u * NT;
+            if (v < V) {
+                bf16x8 y;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) y[j] = (__bf16)acc[u][j];
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, y), dst + v);
+            }
         }
     }
-    const float inv = D > 0.0f ? 1.0f / D : 0.0f;
-    bf16x8 y;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = (__bf16)(acc[j] * inv);
-    o_out[row * G + v] = __builtin_bit_cast(uint4, y);
-    if (v == 0 && lse_out) lse_out[row] = (M == -INFINITY) ? -INFINITY : M + logf(D);
 }
 
 }  // namespace
@@ -68,10 +113,8 @@ hipError_t launch_merge(const void* o_cat, const float* lse_cat, const int32_t* 
                         int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
                         const float* sink, void* o_out, float* lse_out, hipStream_t stream) {
     const int G = D_v / 8;
-    const int64_t n_rows = T_glob * H;
-    const int64_t blocks = (n_rows * G + 255) / 256;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4*)o_cat,
-                       lse_cat, merge_src, P, n_rows, H, G, R_total, sink, (uint4*)o_out, lse_out);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)T_glob), dim3(NT), 0, stream, (const u32x4*)o_cat, lse_cat,
+                       merge_src, P, H, G, R_total, sink, (u32x4*)o_out, lse_out);
     return hipGetLastError();
 }
 

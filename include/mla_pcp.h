@@ -188,7 +188,7 @@ mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
  *  o_out     device bf16 out [T_glob][H][D_v]; lse_out device fp32 [T_glob][H] or NULL.
  * A row with no contributor gets O = 0 and LSE = s_h (-inf without a sink).
  * Errors: INVALID_ARG (null, sizes, P out of 1..64, misalignment); UNSUPPORTED (D_v not
- * a multiple of 8 in 8..1024); HIP.
+ * a multiple of 8 in 8..1024, H above 128); HIP.
  */
 mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
                          int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,

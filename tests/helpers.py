@@ -69,8 +69,8 @@ def compare(name, got_o, got_lse, ref_o, ref_lse, o_tol, lse_tol):
 
 
 def sample_tokens(w, plan, n_random=512, seed=None):
-    """First and last token of every DualChunkSwap chunk (every virtual row of every rank),
-    every decode / replicated token, and n_random uniform tokens."""
+    """First and last token of every DualChunkSwap chunk (every virtual row of every rank;
+    a decode row is a virtual row of one token), and n_random uniform tokens."""
     toks = set()
     for rp in plan.ranks:
         for v in range(rp.n_vrows):

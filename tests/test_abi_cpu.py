@@ -148,3 +148,9 @@ class _Len(_P):
 
     def numel(self):
         return self.n
+
+
+def test_merge_rejects_too_many_heads():
+    f = _P(FAKE)
+    st, _ = _status(lambda: _lib.pcp_lse_merge(f, f, f, 2, 4, 129, 64, 8, None, f, None, stream=0))
+    assert st == _lib.MLA_ERR_UNSUPPORTED

@@ -249,3 +249,29 @@ def test_merge_of_oracle_key_split_partials(gpu_lib, T, P):
     for t in range(T):
         _, _, o, l = oa.attend_keyset(q[t], lat[:t + 1], rope[:t + 1], 0.3, sink.astype(np.float64))
         assert np.max(np.abs(got_o[t] - o)) < O_TOL and np.max(np.abs(lse_out[t].cpu().numpy() - l)) < LSE_TOL
+
+
+def _sampled_run(cfg, n_random):
+    w = synth.workload(cfg)
+    run = DenseRun(w)
+    check_plan(run.pl, run.plan)
+    run.check_insert()
+    toks = hp.sample_tokens(w, run.plan, n_random=n_random)
+    print(f"[check] workload {cfg}: {len(toks)} sampled tokens", flush=True)
+    run.check_values(toks)
+    # every output row finite, on the GPU
+    assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())
+    assert bool(torch.isfinite(run.bufs.o.float()).all()) and bool(torch.isfinite(run.bufs.lse).all())
+    return run
+
+
+def test_dense128k_p4_sampled(gpu_lib):
+    """128K tokens, P=4: plan and insert in full, values on the first/last token of every
+    chunk plus random tokens."""
+    _sampled_run(3, n_random=96)
+
+
+def test_mixed_varlen_decode_sampled(gpu_lib):
+    """8 long prefills + 64 replicated decode rows, P=4: every decode row, the ends of
+    every chunk, and random tokens."""
+    _sampled_run(5, n_random=128)

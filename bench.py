@@ -90,6 +90,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
+                         "(a kernel of known byte count for scaling HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the virtual PCP ranks run "
@@ -188,6 +191,13 @@ def main():
                   "frac_hbm": round(mbytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": mbytes},
         "setup_s": round(setup_s, 1),
     }
+    if args.calib_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, 2048, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -47,7 +47,9 @@ constexpr int BN = 64;   // keys per KV tile (32 per wave of a pair)
 constexpr int NT = 256;  // threads per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescale = 8.0f;  // log2 headroom before the running max is moved
+constexpr float kRescale = 8.0f;
+constexpr int QK_AHEAD = 8;  // Q K^T operand reads kept in flight ahead of the MFMA chain
+constexpr int PV_AHEAD = 4;  // P V MFMAs' worth of V^T reads kept in flight  // log2 headroom before the running max is moved
 
 template <int DL, int DR>
 struct Shape {
@@ -138,37 +140,31 @@ template <class S, int DL, int DR>
 __device__ __forceinline__ void load_tile(char* dst, const char* __restrict__ lat, const char* __restrict__ rope,
                                           int64_t kv0, int kt, int kv_hi, int64_t N_kv, int wave, int lane) {
     constexpr int LV = S::LAT_VECS + 1, RV = S::ROPE_VECS + 1;
+    const int lk = DL * 2 == 1024 ? 0 : lane / LV;            // row of the load this lane fills
+    const int lc = DL * 2 == 1024 ? lane : lane - lk * LV;    // 16-byte chunk inside that row
+    const bool lon = DL * 2 == 1024 || (lc < S::LAT_VECS && lk < S::LAT_ROWS_PER_LOAD);
+    const int rk = lane / RV;
+    const int rc = lane - rk * RV;
+    const bool ron = rc < S::ROPE_VECS && rk < S::ROPE_ROWS_PER_LOAD;
     const int64_t last = min((int64_t)kv_hi - 1, N_kv - 1 - kv0);
-    // latent: row k of the load is lanes [k*LV, k*LV + LAT_VECS)
-    {
-        const int k = DL * 2 == 1024 ? 0 : lane / LV;
-        const int c = DL * 2 == 1024 ? lane : lane - k * LV;
-        const bool on = DL * 2 == 1024 || (c < S::LAT_VECS && k < S::LAT_ROWS_PER_LOAD);
 #pragma unroll
-        for (int i = 0; i < (S::LAT_LOADS + 3) / 4; ++i) {
-            const int n = i * 4 + wave;
-            if (n >= S::LAT_LOADS) break;  // wave-uniform
-            const int r = n * S::LAT_ROWS_PER_LOAD + k;
-            const int64_t j = min((int64_t)kt * BN + r, last);
-            if (DL * 2 == 1024 || (on && r < BN))
-                lds_dma16(lat + (kv0 + j) * (DL * 2) + c * 16, dst + n * S::LAT_ROWS_PER_LOAD * S::LAT_STRIDE);
-        }
+    for (int i = 0; i < (S::LAT_LOADS + 3) / 4; ++i) {
+        const int n = i * 4 + wave;
+        if (n >= S::LAT_LOADS) break;
+        const int r = n * S::LAT_ROWS_PER_LOAD + lk;
+        const int64_t j = min((int64_t)kt * BN + r, last);
+        if (lon && r < BN)
+            lds_dma16(lat + (kv0 + j) * (DL * 2) + lc * 16, dst + n * S::LAT_ROWS_PER_LOAD * S::LAT_STRIDE);
     }
-    // rope: ROPE_ROWS_PER_LOAD rows per load
-    {
-        const int k = lane / RV;
-        const int c = lane - k * RV;
-        const bool on = c < S::ROPE_VECS && k < S::ROPE_ROWS_PER_LOAD;
 #pragma unroll
-        for (int i = 0; i < (S::ROPE_LOADS + 3) / 4; ++i) {
-            const int n = i * 4 + ((wave + 2) & 3);  // start on the waves with fewer latent loads
-            if (n >= S::ROPE_LOADS) break;
-            const int r = n * S::ROPE_ROWS_PER_LOAD + k;
-            const int64_t j = min((int64_t)kt * BN + r, last);
-            if (on && r < BN)
-                lds_dma16(rope + (kv0 + j) * (DR * 2) + c * 16,
-                          dst + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
-        }
+    for (int i = 0; i < (S::ROPE_LOADS + 3) / 4; ++i) {
+        const int n = i * 4 + ((wave + 2) & 3);
+        if (n >= S::ROPE_LOADS) break;
+        const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
+        const int64_t j = min((int64_t)kt * BN + r, last);
+        if (ron && r < BN)
+            lds_dma16(rope + (kv0 + j) * (DR * 2) + rc * 16,
+                      dst + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
     }
 }
 
@@ -189,6 +185,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 
     int v, tile;
     find_tile((int)blockIdx.x, cu, n_vrows, H, sh, v, tile);
+    v = __builtin_amdgcn_readfirstlane(v);  // workgroup-uniform: keep it in SGPRs
+    tile = __builtin_amdgcn_readfirstlane(tile);
     if (v < 0) return;
 
     const int tid = threadIdx.x;
@@ -205,7 +203,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const bool valid = rloc < nrows;
     const int64_t grow = (int64_t)tok0 * H + rloc;  // global row (token-major, then head)
     const int pos = valid ? positions[tok0 + rloc / H] : -1;
-    const int64_t kv0 = vrow_kv_start[v];
+    const int64_t kv0 = __builtin_amdgcn_readfirstlane(vrow_kv_start[v]);
 
     // KV extent of the tile: largest position among its rows, plus one.
     int mp = pos;
@@ -225,7 +223,12 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     int kv_hi = s_maxpos[0];
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) kv_hi = max(kv_hi, s_maxpos[w]);
-    kv_hi += 1;
+    kv_hi = __builtin_amdgcn_readfirstlane(kv_hi + 1);
+    // smallest position among this wave's rows: key blocks at or below it need no mask
+    int pmin = valid ? pos : INT32_MAX;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) pmin = min(pmin, __shfl_xor(pmin, off));
+    pmin = __builtin_amdgcn_readfirstlane(pmin);
 
     constexpr int NB0 = S::NB / 2;  // O column blocks per wave
     f32x16 acc_o[NB0];
@@ -249,6 +252,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     // distinct LDS objects, so the compiler can tell that the streaming loads never
     // touch the tile being read and does not wait for them.
     auto tile_step = [&](const char* kvt, char* nxt, int kt) {
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) asm volatile("" : "+a"(qf[kb]));
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
         __syncthreads();                     // ... and every wave's; the other buffer is free
         if (kt + 1 < n_tiles) load_tile<S, DL, DR>(nxt, lat, rope, kv0, kt + 1, kv_hi, N_kv, wave, lane);
@@ -257,32 +262,46 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         {
             const char* kl = kvt + k_lat_off;
             const char* kr = kvt + k_rope_off;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < S::KB; ++kb) {
                 const char* ap = kb < DL / 16 ? kl + kb * 32 : kr + (kb - DL / 16) * 32;
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
             }
-        }
-        float mloc = -INFINITY;
-        const int key0 = kt * BN + 32 * side + 4 * half;  // key of s[0]
+            // Keep QK_AHEAD operand reads in flight ahead of the MFMA chain.
+            constexpr int AHEAD = S::KB < QK_AHEAD ? S::KB : QK_AHEAD;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int j = key0 + 8 * (i >> 2) + (i & 3);
-            const float x = j <= pos ? s[i] * scale_log2 : -INFINITY;
-            s[i] = x;
-            mloc = fmaxf(mloc, x);
+            for (int kb = 0; kb < S::KB - AHEAD; ++kb) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));  // max over this wave's 32 keys
+        const int key0 = kt * BN + 32 * side + 4 * half;  // key of s[0]
+        if (kt * BN + 32 * side + 31 > pmin) {  // wave-uniform: a causal diagonal crosses these keys
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = key0 + 8 * (i >> 2) + (i & 3) <= pos ? s[i] : -INFINITY;
+        }
+        float smax = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) smax = fmaxf(smax, s[i]);
+        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        const float mloc = smax * scale_log2;  // max over this wave's 32 keys (log2 units)
         // Fast path: P against the current reference, published with a "needs a new
         // reference" flag; the slow path (any wave flagged) agrees on the pair max first.
         const bool need = mloc > m_ref + kRescale;
         float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+        float pf[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -m_use));
         bf16x8 pk[2];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            pk[0][j] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_use);
-            pk[1][j] = (__bf16)__builtin_amdgcn_exp2f(s[8 + j] - m_use);
+            pk[0][j] = (__bf16)pf[j];
+            pk[1][j] = (__bf16)pf[8 + j];
         }
         Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
         Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
@@ -304,9 +323,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 #pragma unroll
             for (int d = 0; d < NB0; ++d) acc_o[d] *= alpha;
 #pragma unroll
+            for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -m_use));
+#pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pk[0][j] = (__bf16)__builtin_amdgcn_exp2f(s[j] - m_use);
-                pk[1][j] = (__bf16)__builtin_amdgcn_exp2f(s[8 + j] - m_use);
+                pk[0][j] = (__bf16)pf[j];
+                pk[1][j] = (__bf16)pf[8 + j];
             }
             __syncthreads();  // everyone has read the flags and the fast-path P
             Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
@@ -315,7 +336,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         }
         float lsum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) lsum += __builtin_amdgcn_exp2f(s[i] - m_use);
+        for (int i = 0; i < 16; ++i) lsum += pf[i];
         l_run += lsum;
         // P^T fragments: our two key blocks (tile rows 32*side + [0,32)) and the partner's
         // (rows 32*(1-side) + [0,32)); the matching V rows are picked by address.
@@ -325,6 +346,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         // O^T[dim, row] += V^T[dim, key] P^T[key, row] over this wave's column blocks.
         // Element j of the lane's k-slice of a 16-key block is key
         // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
+        __builtin_amdgcn_sched_barrier(0);
         const char* v_own = kvt + v_off + (32 * side) * S::LAT_STRIDE;
         const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * S::LAT_STRIDE;
 #pragma unroll
@@ -338,6 +360,19 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
                 const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
                 acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);
             }
+        }
+        {
+            // two transposing reads per MFMA, PV_AHEAD MFMAs' worth of reads in flight
+            constexpr int NM = NB0 * 4;
+            constexpr int AHEAD = NM < PV_AHEAD ? NM : PV_AHEAD;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+            for (int m = 0; m < NM - AHEAD; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

@@ -42,6 +42,25 @@ def merge_bytes(merge_src: np.ndarray, H: int, Dv: int) -> float:
     return float(n_contrib * H * (2 * Dv + 4) + T * H * (2 * Dv + 4) + T * P * 4)
 
 
+def measured_traffic(workload: int):
+    """HBM bytes per launch of the attention and merge kernels from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy kernel), or None when the kernel
+    sources have changed since those counters were taken (or for other workloads)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "dense_attention_128k_p4_traffic.json")
+    if workload != 3 or not os.path.exists(path):
+        return None, None
+    rec = json.load(open(path))
+
+    def sha(name):
+        with open(os.path.join(ROOT, "context_mla_prefill_amd", "csrc", name), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()[:16]
+
+    att = rec["bytes_per_launch"] if sha("attn_dense.hip") == rec["kernel_source_sha256_prefix"] else None
+    mer = rec["merge_bytes_per_launch"] if sha("merge.hip") == rec["merge_source_sha256_prefix"] else None
+    return att, mer
+
+
 def cpu_baseline(w, n_tokens: int, seconds: float):
     """Time the oracle on a bounded sample of query tokens (their full key sets)."""
     from oracle import attention as oa
@@ -171,6 +190,7 @@ def main():
     avg_launch_ms = float(np.mean(t_rank))
     achieved = (flops_step / w.P) / (avg_launch_ms * 1e-3) / 1e12
     mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl)
+    att_traffic, merge_traffic = measured_traffic(args.workload)
 
     out = {
         "metric": "PCP-shard MLA prefill attention TFLOP/s + MFMA% at 1 GPU; merge GB/s",
@@ -182,13 +202,14 @@ def main():
         "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
                    "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": att_traffic},
         "attention": {"rank_ms": [round(x, 3) for x in t_rank],
                       "rank_tflops": [round(f / (t * 1e-3) / 1e12, 2) for f, t in zip(flops_r, t_rank)],
                       "balance_last_over_first": round(t_rank[-1] / t_rank[0], 4),
                       "tokens_per_s": round(w.T_glob / (ms_step * 1e-3), 1)},
         "merge": {"ms": round(t_merge, 4), "GB/s": round(mbytes / (t_merge * 1e-3) / 1e9, 1),
-                  "frac_hbm": round(mbytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": mbytes},
+                  "frac_hbm": round(mbytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": mbytes,
+                  "traffic": merge_traffic},
         "setup_s": round(setup_s, 1),
     }
     if args.calib_copy:

@@ -34,6 +34,24 @@ def attn_flops(positions: np.ndarray, H: int, Dl: int, Dr: int) -> float:
     return float(2 * (Dl + Dr + Dl) * H) * float((positions.astype(np.int64) + 1).sum())
 
 
+def sparse_set_sizes(topk_rows: np.ndarray, w) -> np.ndarray:
+    """|key set| per global token: selected indices in [0, p] outside the window, plus the
+    window keys [max(0, p-window+1), p]."""
+    cu = np.zeros(w.n_req + 1, np.int64)
+    cu[1:] = np.cumsum(w.q_lens)
+    t = np.arange(w.T_glob)
+    b = np.searchsorted(cu, t, side="right") - 1
+    p = (w.kv_lens[b] - w.q_lens[b] + (t - cu[b])).astype(np.int64)
+    lo = np.maximum(0, p - w.window + 1)
+    out = np.empty(w.T_glob, np.int64)
+    for a in range(0, w.T_glob, 8192):
+        e = topk_rows[a:a + 8192].astype(np.int64)
+        pp_, lo_ = p[a:a + 8192, None], lo[a:a + 8192, None]
+        ok = (e >= 0) & (e <= pp_) & ((e < lo_) if w.window > 0 else True)
+        out[a:a + 8192] = ok.sum(1) + (p[a:a + 8192] - lo[a:a + 8192] + 1 if w.window > 0 else 0)
+    return out
+
+
 def merge_bytes(merge_src: np.ndarray, H: int, Dv: int) -> float:
     """Bytes the merge must move: each contributor row (O bf16 + LSE fp32) read, each
     output row written, plus the map."""
@@ -124,27 +142,34 @@ def main():
 
     _lib.load()
     w = synth.workload(args.workload)
-    if w.topk:
-        raise SystemExit("the sparse workload is not wired into bench.py yet")
     dev = "cuda"
+    sparse = w.topk > 0
 
     def upload(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     t_setup = time.perf_counter()
     q = upload(synth.q_rows(w))
-    lat_full = upload(synth.latent_rows(w))
+    if sparse:
+        lat_full = torch.from_numpy(synth.latent_rows(w)).to(dev)
+        kv_scale = torch.from_numpy(synth.kv_scales(w)).to(dev)
+        topk_host = synth.topk_rows(w)
+        topk = torch.from_numpy(topk_host).to(dev)
+    else:
+        lat_full = upload(synth.latent_rows(w))
+        kv_scale, topk, topk_host = None, None, None
     rope_full = upload(synth.rope_rows(w))
     sink = torch.from_numpy(synth.sink(w)).to(dev)
     pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
     pp.run_partition(pl)
-    ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full) for r in range(w.P)]
+    ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk) for r in range(w.P)]
     del q
     kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
     kv_rope = rope_full.clone()
     bufs = pp.alloc_step(pl, w.H, w.Dl)
-    args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale)
-              for r in range(w.P)]
+    kv_dtype = _lib.MLA_KV_FP8_E4M3 if sparse else _lib.MLA_KV_BF16
+    args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, kv_dtype=kv_dtype,
+                              kv_scale=kv_scale, topk=w.topk, window=w.window) for r in range(w.P)]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -157,7 +182,7 @@ def main():
         pp.run_partition(pl)
         for r in range(w.P):
             _lib.pcp_kv_insert(ranks[r].latent, ranks[r].rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
-                               _lib.MLA_KV_BF16, w.N_kv, kv_lat, kv_rope)
+                               kv_dtype, w.N_kv, kv_lat, kv_rope)
         for r in range(w.P):
             if ev:
                 ev[r][0].record(stream)
@@ -182,7 +207,12 @@ def main():
 
     # algorithmic work from the device plan's own positions
     pos_r = [pl.positions[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
-    flops_r = [attn_flops(p, w.H, w.Dl, w.Dr) for p in pos_r]
+    if sparse:
+        n_keys = sparse_set_sizes(topk_host, w)
+        gidx_r = [pl.local_gidx[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
+        flops_r = [float(2 * (w.Dl + w.Dr + w.Dl) * w.H) * float(n_keys[g].sum()) for g in gidx_r]
+    else:
+        flops_r = [attn_flops(p, w.H, w.Dl, w.Dr) for p in pos_r]
     flops_step = float(sum(flops_r))
     t_rank = [float(np.mean([events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)]))
               for r in range(w.P)]
@@ -197,7 +227,8 @@ def main():
         "value": round(flops_step / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3 KV dequantised to bf16, bf16 MFMA" if sparse else "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 bf16 q/latent/rope, N(0,1) sink)",
         "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
                    "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU"},
@@ -219,7 +250,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not sparse:  # the oracle baseline is timed on the dense workload
         out["cpu_baseline"] = cpu_baseline(w, 2048, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

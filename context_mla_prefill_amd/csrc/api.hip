@@ -143,9 +143,9 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: topk=%d outside 0..2048", a->topk);
         if (a->window < 0 || a->window > 4096)
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: window=%d outside 0..4096", a->window);
-        if (!big || a->kv_dtype != MLA_KV_FP8_E4M3 || a->H % 32 != 0)
+        if (!big || a->kv_dtype != MLA_KV_FP8_E4M3 || a->H % 64 != 0)
             return fail(MLA_ERR_UNSUPPORTED,
-                        "mla_prefill_partial: sparse path needs 512+64 dims, fp8 KV and H %% 32 == 0");
+                        "mla_prefill_partial: sparse path needs 512+64 dims, fp8 KV and H %% 64 == 0");
     } else if (a->kv_dtype != MLA_KV_BF16) {
         return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: dense path takes bf16 KV");
     }

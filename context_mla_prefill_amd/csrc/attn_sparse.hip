@@ -1,0 +1,227 @@
+// Rank-local sparse MLA partial attention: top-k selected keys plus a sliding window,
+// latent KV stored as fp8-e4m3 with one fp32 scale per 64 packed KV rows.
+//
+// Each PCP rank computes a local partial attention whose LSE/output are merged later with
+// the sink applied once ("[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid
+// KV and MegaMoE", "Purpose": PCP merge for sparse prefill attention); the fp8 MLA cache
+// with block size 64 is the one named in "[Feature][PCP] Add DeepSeek-V4.1-Flash
+// support", "vLLM Launch Arguments" (the layout is this library's: E4M3FN codes, one
+// fp32 scale per 64 packed rows, rope kept bf16).
+//
+// Key set of a query at position p (request-relative): the selected indices that lie in
+// [0, p] and outside the window, plus every window key [max(0, p-window+1), p]; a selected
+// index inside the window is counted once (the window supplies it). Selected indices must
+// be distinct; -1 (or anything outside [0, p]) is a pad.
+//
+// Work decomposition: one workgroup per (token, 64 heads), i.e. the same 64 rows and wave
+// pairs as the dense kernel, running the same per-tile compute. A tile is 64 key slots:
+// first the selected-index slots in 64-wide groups (a group with no valid key is skipped),
+// then the window. Per tile:
+//   * the fp8 rows of the tile's keys are gathered HBM -> LDS staging by direct-to-LDS
+//     loads (two keys per wave-wide load) while the previous tile computes;
+//   * the workgroup dequantises the staged rows once into the padded bf16 tile,
+//     bf16_rne(fp32(e4m3) * scale[row/64]);
+//   * rope rows stream straight into the tile once every wave is done with the previous
+//     tile's Q K^T reads.
+#include "attn_core.h"
+
+namespace mla {
+namespace {
+
+using namespace attn;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int MAX_TOPK = 2048;
+
+template <int DL, int DR>
+__global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
+    const __bf16* __restrict__ q, const uint8_t* __restrict__ lat8, const float* __restrict__ kv_scale,
+    const char* __restrict__ rope, const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
+    const int32_t* __restrict__ positions, const int32_t* __restrict__ topk_idx, int topk, int window,
+    int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
+    using S = Shape<DL, DR>;
+    static_assert(DL == 512, "the fp8 staging assumes 512-byte latent rows");
+    __shared__ __attribute__((aligned(1024))) char kv_tile[S::TILE_BYTES];  // dequantised bf16 tile
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[BN * DL];       // fp8 rows of the next tile
+    __shared__ float stage_scale[BN];
+    __shared__ int sel[MAX_TOPK];            // this token's selected indices
+    __shared__ uint64_t tmask[2];            // valid-key bits of the current / next tile
+    __shared__ Exchange ex;
+
+    const int hg_count = H / BM;
+    const int tok = blockIdx.x / hg_count;
+    const int hg = blockIdx.x - tok * hg_count;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int pair = wave >> 1;
+    const int side = wave & 1;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int l32 = lane & 31;
+
+    // virtual row of this token: last v with cu[v] <= tok
+    int lo_v = 0, hi_v = n_vrows;
+    while (hi_v - lo_v > 1) {
+        const int mid = (lo_v + hi_v) >> 1;
+        if (cu[mid] <= tok) lo_v = mid; else hi_v = mid;
+    }
+    const int64_t kv0 = vrow_kv_start[lo_v];
+    const int p = positions[tok];
+    const int head = hg * BM + pair * 32 + l32;
+    const int64_t grow = (int64_t)tok * H + head;
+    const int64_t last_row = N_kv - 1;
+
+    for (int i = tid; i < MAX_TOPK; i += NT) sel[i] = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
+
+    bf16x8 qf[S::KB];
+    {
+        const __bf16* qrow = q + grow * S::DQK + 8 * half;
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qrow + kb * 16);
+    }
+    __syncthreads();
+
+    const int win_lo = max(0, p - window + 1);  // first window key (window > 0)
+    const int n_sel_tiles = (topk + BN - 1) / BN;
+    const int n_tiles = n_sel_tiles + (window + BN - 1) / BN;
+
+    // Key of slot j of tile t (request-relative) and whether the slot holds a key of the set.
+    auto slot_key = [&](int t, int j, bool& ok) -> int {
+        if (t < n_sel_tiles) {
+            const int e = sel[t * BN + j];
+            ok = e >= 0 && e <= p && (window == 0 || e < win_lo);
+            return ok ? e : 0;
+        }
+        const int w = (t - n_sel_tiles) * BN + j;
+        const int k = win_lo + w;
+        ok = window > 0 && w < window && k <= p;
+        return ok ? k : 0;
+    };
+    // Next tile index >= t that holds at least one key (n_tiles if none); workgroup-uniform.
+    auto next_live = [&](int t) -> int {
+        for (; t < n_tiles; ++t) {
+            bool ok = false;
+            if (lane < BN) slot_key(t, lane, ok);
+            if (__ballot(ok)) break;  // every wave evaluates the same slots
+        }
+        return t;
+    };
+    // Gathers tile t: fp8 latent rows and their scales into staging, its valid-key bits.
+    auto gather_latent = [&](int t, int mslot) {
+        // wave-wide load n moves keys 2n and 2n+1 (32 lanes x 16 bytes each)
+#pragma unroll
+        for (int i = 0; i < BN / 2 / 4; ++i) {
+            const int n = i * 4 + wave;
+            const int j = 2 * n + half;
+            bool ok;
+            const int64_t row = min(kv0 + slot_key(t, j, ok), last_row);
+            lds_dma16(lat8 + row * DL + l32 * 16, (char*)stage + n * 1024);
+        }
+        if (wave == 0) {
+            bool ok;
+            const int64_t row = min(kv0 + slot_key(t, lane, ok), last_row);
+            stage_scale[lane] = kv_scale[row >> 6];
+            const uint64_t bits = __ballot(ok);
+            if (lane == 0) tmask[mslot] = bits;
+        }
+    };
+    // Rope rows of tile t straight into the bf16 tile (7 rows of 144 bytes per load).
+    auto gather_rope = [&](int t) {
+        constexpr int RV = S::ROPE_VECS + 1;
+        const int rk = lane / RV;
+        const int rc = lane - rk * RV;
+        const bool ron = rc < S::ROPE_VECS && rk < S::ROPE_ROWS_PER_LOAD;
+#pragma unroll
+        for (int i = 0; i < (S::ROPE_LOADS + 3) / 4; ++i) {
+            const int n = i * 4 + wave;
+            if (n >= S::ROPE_LOADS) break;  // wave-uniform
+            const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
+            bool ok;
+            const int64_t row = min(kv0 + slot_key(t, r < BN ? r : 0, ok), last_row);
+            if (ron && r < BN)
+                lds_dma16(rope + row * (DR * 2) + rc * 16, kv_tile + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
+        }
+    };
+    // Dequantises the staged fp8 rows into the bf16 tile: thread handles 16-byte chunks
+    // tid, tid+256, ... (consecutive lanes read consecutive LDS bytes).
+    auto dequant = [&]() {
+#pragma unroll
+        for (int i = 0; i < BN * DL / 16 / NT; ++i) {
+            const int k = i * NT + tid;
+            const int r = k / (DL / 16);
+            const int c = k - r * (DL / 16);
+            const uint4 raw = *reinterpret_cast<const uint4*>(stage + k * 16);
+            const float sc = stage_scale[r];
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            bf16x8 o0, o1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[u], false);
+                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[u], true);
+                const int e = 4 * u;
+                bf16x8& o = e < 8 ? o0 : o1;
+                const int f = e & 7;
+                o[f] = (__bf16)(a.x * sc);
+                o[f + 1] = (__bf16)(a.y * sc);
+                o[f + 2] = (__bf16)(b.x * sc);
+                o[f + 3] = (__bf16)(b.y * sc);
+            }
+            char* dst = kv_tile + r * S::LAT_STRIDE + c * 32;
+            *reinterpret_cast<bf16x8*>(dst) = o0;
+            *reinterpret_cast<bf16x8*>(dst + 16) = o1;
+        }
+    };
+
+    constexpr int NB0 = S::NB / 2;
+    f32x16 acc_o[NB0];
+#pragma unroll
+    for (int d = 0; d < NB0; ++d) acc_o[d] = f32x16{};
+    float m_ref = -INFINITY;
+    float l_run = 0.0f;
+    const LaneOffsets<S> lo(side, lane);
+
+    int t = next_live(0);
+    int ms = 0;
+    if (t < n_tiles) {
+        gather_latent(t, ms);
+        gather_rope(t);
+    }
+    while (t < n_tiles) {
+#pragma unroll
+        for (int kb = 0; kb < S::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gathers of tile t landed
+        __syncthreads();                     // ... and every wave's
+        dequant();
+        __syncthreads();  // bf16 tile complete; staging free
+        const uint64_t bits = tmask[ms];
+        const int tn = next_live(t + 1);
+        if (tn < n_tiles) gather_latent(tn, ms ^ 1);
+        auto keymask = [&](f32x16& s) {
+            const int key0 = 32 * side + 4 * half;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                s[i] = (bits >> (key0 + 8 * (i >> 2) + (i & 3))) & 1 ? s[i] : -INFINITY;
+        };
+        auto rope_next = [&] {
+            if (tn < n_tiles) gather_rope(tn);
+        };
+        tile_compute<S, DL>(kv_tile, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex, keymask, rope_next);
+        t = tn;
+        ms ^= 1;
+    }
+    write_rows<S, DL>(acc_o, m_ref, l_run, true, grow, wave, side, lane, ex, o_out, lse_out);
+}
+
+}  // namespace
+
+hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream) {
+    const int64_t grid = (int64_t)a.T_loc * (a.H / BM);
+    hipLaunchKernelGGL((sparse_partial_kernel<512, 64>), dim3((unsigned)grid), dim3(NT), 0, stream,
+                       (const __bf16*)a.q, (const uint8_t*)a.latent_kv, a.kv_scale, (const char*)a.rope_k,
+                       a.cu_seqlens_q, a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H,
+                       a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse);
+    return hipGetLastError();
+}
+
+}  // namespace mla

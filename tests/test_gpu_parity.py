@@ -275,3 +275,113 @@ def test_mixed_varlen_decode_sampled(gpu_lib):
     """8 long prefills + 64 replicated decode rows, P=4: every decode row, the ends of
     every chunk, and random tokens."""
     _sampled_run(5, n_random=128)
+
+
+# ----------------------------------------------------------------------------- sparse fp8
+
+SPARSE_O_TOL = 3e-2
+
+
+class SparseRun:
+    """partition -> fp8 insert -> P sparse partials -> merge for an fp8 top-k workload."""
+
+    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None):
+        self.w = w
+        self.plan = hp.oracle_plan(w)
+        print(f"[run] sparse workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
+        self.q_bits = synth.q_rows(w)
+        self.lat_codes = synth.latent_rows(w) if lat_codes is None else lat_codes
+        self.kv_scale = synth.kv_scales(w) if kv_scale is None else kv_scale
+        self.rope_bits = synth.rope_rows(w)
+        self.topk = synth.topk_rows(w) if topk_rows is None else topk_rows
+        self.sink = synth.sink(w)
+        q = dev_bf16(self.q_bits)
+        lat_full = torch.from_numpy(np.ascontiguousarray(self.lat_codes)).cuda()
+        rope_full = dev_bf16(self.rope_bits)
+        topk_d = torch.from_numpy(np.ascontiguousarray(self.topk)).cuda()
+        scale_d = torch.from_numpy(np.ascontiguousarray(self.kv_scale, dtype=np.float32)).cuda()
+        self.pl = pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+        pp.run_partition(pl)
+        # Full KV with every new-token row poisoned (NaN codes); the inserts must restore it.
+        self.kv_lat, self.kv_rope = lat_full.clone(), rope_full.clone()
+        new_rows = torch.unique(pl.slot.long())
+        self.kv_lat[new_rows] = 0x7F
+        self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl)
+        self.sink_d = torch.from_numpy(self.sink).cuda()
+        ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk_d) for r in range(w.P)]
+        for r, ri in enumerate(ranks):
+            _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
+                               _lib.MLA_KV_FP8_E4M3, w.N_kv, self.kv_lat, self.kv_rope)
+        for r, ri in enumerate(ranks):
+            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk, window=w.window)
+            _lib.mla_prefill_partial(args)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl)
+        torch.cuda.synchronize()
+        self.lat_full, self.rope_full = lat_full, rope_full
+
+    def check_insert(self):
+        assert torch.equal(self.kv_lat, self.lat_full)
+        assert torch.equal(self.kv_rope.view(torch.int16), self.rope_full.view(torch.int16))
+
+    def check_values(self, tokens, o_tol=SPARSE_O_TOL):
+        w, plan = self.w, self.plan
+        ref = hp.oracle_sparse(w, plan, self.q_bits, self.lat_codes, self.kv_scale, self.rope_bits, self.topk,
+                               self.sink, tokens)
+        o_cat = on.bf16_to_f64(host_bits(self.bufs.o_cat))
+        lse_cat = self.bufs.lse_cat.cpu().numpy()
+        tokset = set(int(t) for t in tokens)
+        for r, rp in enumerate(plan.ranks):
+            rows = [i for i, g in enumerate(rp.local_gidx) if int(g) in tokset]
+            if not rows:
+                continue
+            gi = [int(rp.local_gidx[i]) for i in rows]
+            cat = plan.row_off[r] + np.asarray(rows)
+            hp.compare(f"sparse workload {w.cfg} rank {r} partial", o_cat[cat], lse_cat[cat],
+                       np.stack([ref[g][0] for g in gi]), np.stack([ref[g][1] for g in gi]), o_tol, LSE_TOL)
+        toks = np.asarray(sorted(tokset))
+        o = on.bf16_to_f64(host_bits(self.bufs.o))[toks]
+        lse = self.bufs.lse.cpu().numpy()[toks]
+        hp.compare(f"sparse workload {w.cfg} merged", o, lse, np.stack([ref[g][2] for g in toks]),
+                   np.stack([ref[g][3] for g in toks]), o_tol, LSE_TOL)
+
+
+def test_fp8_dequant_bit_exact(gpu_lib):
+    """A query whose key set is one key returns that key's dequantised latent row exactly:
+    every finite E4M3FN code, times a non-power-of-two scale, rounded to bf16."""
+    w = synth.custom(201, [1], [1], P=1, H=64, Dl=512, Dr=64, topk=64, window=128, kv_dtype="fp8",
+                     latent_std=1.0)
+    codes = np.arange(512, dtype=np.int64) % 256
+    codes[(codes & 0x7F) == 0x7F] = 0  # the two NaN codes
+    lat = codes.astype(np.uint8)[None, :]
+    scale = np.array([0.3713], np.float32)
+    run = SparseRun(w, lat_codes=lat, kv_scale=scale, topk_rows=np.full((1, 64), -1, np.int32))
+    got = on.bf16_to_f64(host_bits(run.bufs.o_cat)[0])  # [H, 512]
+    want = on.dequant_fp8_rows(lat, np.array([0]), scale)[0]
+    bad = np.nonzero(got != want[None, :])
+    assert len(bad[0]) == 0, f"codes {codes[bad[1][:8]]}: got {got[bad][:8]} want {want[bad[1][:8]]}"
+    # exact equality of values (the sign of a zero is not carried through P V: +0 + -0 = +0)
+
+
+def test_sparse_small_all_rows(gpu_lib):
+    """Selected keys + window on a small fp8 workload: every row of both ranks."""
+    w = synth.custom(202, [1500, 700], [1500, 900], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,
+                     kv_dtype="fp8", latent_std=1.0)
+    run = SparseRun(w)
+    check_plan(run.pl, run.plan)
+    run.check_insert()
+    run.check_values(np.arange(w.T_glob))
+
+
+def test_sparse128k_p2_sampled(gpu_lib):
+    """128K tokens, P=2, 64 heads, top-2048 + window 128, fp8 KV: plan and insert in full,
+    values on the ends of every chunk plus random tokens, all rows finite."""
+    w = synth.workload(4)
+    run = SparseRun(w)
+    check_plan(run.pl, run.plan)
+    run.check_insert()
+    toks = hp.sample_tokens(w, run.plan, n_random=64)
+    print(f"[check] sparse workload 4: {len(toks)} sampled tokens", flush=True)
+    run.check_values(toks)
+    assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())

@@ -1,8 +1,9 @@
 // Shared pieces of the MLA partial-attention kernels (dense causal and top-k sparse):
-// tile geometry, the direct-to-LDS load, and the per-tile compute on one LDS-resident
-// KV tile (transposed Q K^T, online softmax with a lazy reference max, the wave-pair P
-// exchange, transposed P V). Both kernels run exactly this arithmetic; they differ in
-// which keys a tile holds and how a tile reaches LDS.
+// fragment types, the workgroup shape, the key-row permutation of an LDS tile, the
+// direct-to-LDS load, and the per-tile compute on one LDS-resident KV tile (transposed
+// Q K^T, online softmax with a lazy reference max, the wave-pair P exchange, transposed
+// P V) used by the sparse kernel. The dense kernel runs the same per-tile arithmetic in
+// its own copy, whose Q K^T section also issues the next tile's loads between MFMAs.
 #pragma once
 
 #include <math.h>
@@ -64,23 +65,38 @@ struct Exchange {
     int flag[NT / 64];         // "needs a new reference max" per wave
 };
 
+// Score row -> LDS key row. Inside every block of 16 keys, score row r lives in LDS row
+// kperm(r) = 4*(r%4) + 2*((r/8)%2) + (r/4)%2. With the 1040-byte row stride (an odd number
+// of 16-byte bank slots) this makes both read patterns bank-conflict free: the Q K^T row
+// reads (16 lanes on 16 distinct rows of a block) and the transposing V^T reads (each
+// 16-lane group reads the 4 key rows one tr-read covers, which kperm places 4 rows apart).
+__device__ __forceinline__ constexpr int kperm(int r) { return 4 * (r & 3) + 2 * ((r >> 3) & 1) + ((r >> 2) & 1); }
+
+// Tile key (0..63) of score s[i] of a lane in half `half` of wave side `side`: score row
+// m = 8*(i/4) + 4*half + i%4 of this wave's 32 rows.
+__device__ __forceinline__ int score_key(int side, int half, int i) {
+    return 32 * side + 16 * (i >> 3) + kperm(8 * ((i >> 2) & 1) + 4 * half + (i & 3));
+}
+
 // Per-lane LDS offsets inside a tile (everything else is an immediate):
-//  * Q K^T reads: key row 32*side + l32, 8 elements at 8*half of each 16-wide k-block;
-//  * V^T reads: key row 4*half + (lane%16)/4 (+16 kb, +8), dims 16*((lane/16)%2) + 4*(lane%4).
+//  * Q K^T reads: LDS row of score row l32, 8 elements at 8*half of each 16-wide k-block;
+//  * V^T reads (first of the two per MFMA): LDS row of score row 4*half + (lane%16)/4 of
+//    the key block, dims 16*((lane/16)%2) + 4*(lane%4); the second read is 2 rows further.
 template <class S>
 struct LaneOffsets {
     int k_lat, k_rope, v;
     __device__ __forceinline__ LaneOffsets(int side, int lane) {
         const int half = lane >> 5, l32 = lane & 31;
-        k_lat = (32 * side + l32) * S::LAT_STRIDE + 16 * half;
-        k_rope = S::ROPE_OFF + (32 * side + l32) * S::ROPE_STRIDE + 16 * half;
-        v = (4 * half + ((lane & 15) >> 2)) * S::LAT_STRIDE + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+        const int krow = 32 * side + 16 * (l32 >> 4) + kperm(l32 & 15);
+        k_lat = krow * S::LAT_STRIDE + 16 * half;
+        k_rope = S::ROPE_OFF + krow * S::ROPE_STRIDE + 16 * half;
+        v = kperm(4 * half + ((lane & 15) >> 2)) * S::LAT_STRIDE + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     }
 };
 
 // Scores, softmax and P V of one LDS-resident tile for this wave.
-//  mask(s):          applies -inf to scores of keys the row must not see (s[i] is key
-//                    32*side + 8*(i/4) + 4*half + i%4 of the tile, for row l32);
+//  mask(s):          applies -inf to scores of keys the row must not see (s[i] is tile
+//                    key score_key(side, half, i), for row l32);
 //  after_exchange(): runs right after the barrier that publishes the P fragments, when
 //                    every wave has finished its Q K^T reads of this tile.
 template <class S, int DL, class Mask, class Hook>
@@ -184,7 +200,7 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
         for (int kb = 0; kb < 4; ++kb) {
             const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * S::LAT_STRIDE + (side * NB0 + d) * 64;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 8 * S::LAT_STRIDE));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * S::LAT_STRIDE));
             const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
             acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);

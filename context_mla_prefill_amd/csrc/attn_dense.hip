@@ -14,13 +14,15 @@
 //    Q of those rows in registers for the whole KV loop.
 //  * KV tiles of BN = 64 keys move HBM -> LDS with direct-to-LDS loads into a double
 //    buffer (the next tile streams in while the current one is used) and are shared by
-//    all heads and waves. 16-byte chunks are XOR-swizzled by row to spread LDS banks.
+//    all heads and waves. For the 512+64 shape the loads of the next tile are spread
+//    over the Q K^T MFMAs of the current one (two MFMAs apart), so the CU's vector
+//    memory pipe drains them while the matrix core runs instead of stalling the wave.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, A = K from
 //    LDS, B = Q^T from registers); wave s of a pair scores keys [32 s, 32 s + 32) of the
 //    tile. Each lane then holds scores of ONE query row, so the row max needs one
 //    cross-half exchange and the running sum stays per lane until the epilogue.
 //  * The output is accumulated transposed, O^T += V^T P^T; wave s of a pair owns output
-//    columns [256 s, 256 s + 256) and needs P for all 64 keys, so the two waves swap
+//    columns [DL/2 s, DL/2 s + DL/2) and needs P for all 64 keys, so the two waves swap
 //    their bf16 P fragments through LDS. The P fragment is the score accumulator
 //    re-packed in place; V^T comes from transposing LDS reads (ds_read_b64_tr_b16) in
 //    the key order the score layout gives each lane.
@@ -36,6 +38,42 @@ namespace mla {
 namespace {
 
 using namespace attn;
+
+// LDS image of one KV tile of the dense kernel.
+//  * Latent rows at a stride of DL*2 + 16 bytes; inside every block of 16 keys, key
+//    (score row) r sits in LDS row kperm(r) (conflict-free Q K^T and V^T reads).
+//  * 512+64 ("wide"): one latent row per direct-to-LDS load, so the source row of a
+//    load is wave-uniform and its address scalar. Rope rows are packed 8 per load at
+//    128 bytes with no pad; the 16-byte chunk c of row r is stored at chunk
+//    c ^ ((r / 2) % 8), which keeps the Q K^T rope reads conflict-free.
+//  * Other shapes: several latent rows per load, rope rows at a stride of DR*2 + 16,
+//    loads predicated per lane (no interleaving).
+template <int DL, int DR>
+struct DenseTile {
+    static constexpr bool WIDE = DL * 2 == 1024 && DR * 2 == 128;
+    static constexpr int DQK = DL + DR;
+    static constexpr int KB = DQK / 16;  // 16-wide k-blocks of Q K^T
+    static constexpr int NB = DL / 32;   // 32-wide column blocks of O
+    static constexpr int LAT_VECS = DL / 8;
+    static constexpr int ROPE_VECS = DR / 8;
+    static constexpr int LAT_STRIDE = DL * 2 + 16;
+    static constexpr int ROPE_STRIDE = WIDE ? DR * 2 : DR * 2 + 16;
+    static constexpr int ROPE_OFF = BN * LAT_STRIDE;
+    static constexpr int TILE_BYTES = ROPE_OFF + BN * ROPE_STRIDE;
+    static constexpr int LAT_ROWS_PER_LOAD = WIDE ? 1 : 64 / (LAT_VECS + 1);
+    static constexpr int ROPE_ROWS_PER_LOAD = WIDE ? 8 : 64 / (ROPE_VECS + 1);
+    static constexpr int LAT_LOADS = (BN + LAT_ROWS_PER_LOAD - 1) / LAT_ROWS_PER_LOAD;
+    static constexpr int ROPE_LOADS = (BN + ROPE_ROWS_PER_LOAD - 1) / ROPE_ROWS_PER_LOAD;
+    // wide shape: every wave issues LAT_PER_WAVE latent and ROPE_PER_WAVE rope loads of
+    // the next tile, one after every LOAD_GAP-th Q K^T MFMA (the last few, which find
+    // no slot there, go among the final MFMAs of the chain)
+    static constexpr int LAT_PER_WAVE = LAT_LOADS / 4;    // 16
+    static constexpr int ROPE_PER_WAVE = ROPE_LOADS / 4;  // 2
+    static constexpr int LOADS_PER_WAVE = LAT_PER_WAVE + ROPE_PER_WAVE;
+    static constexpr int LOAD_GAP = 2;
+    static_assert(DQK % 16 == 0 && DL % 32 == 0 && DR % 8 == 0, "tile shape");
+    static_assert(!WIDE || (LAT_LOADS % 4 == 0 && ROPE_LOADS % 4 == 0), "wide loads split evenly over 4 waves");
+};
 
 __device__ __forceinline__ int block_scan_incl(int v, int* sh) {
     const int t = threadIdx.x;
@@ -86,39 +124,60 @@ __device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ 
     tile_out = s_tile;
 }
 
-// Issues the direct-to-LDS loads of KV tile kt (keys [kt*BN, kt*BN+BN) of the request)
-// into `dst`. A load writes 64 consecutive 16-byte LDS chunks, one per lane; lanes that
-// would land on a row pad are switched off. Keys past the tile's extent repeat the last
-// valid row (finite values; their scores are masked). Wave w issues loads w, w+4, ...
-template <class S, int DL, int DR>
-__device__ __forceinline__ void load_tile(char* dst, const char* __restrict__ lat, const char* __restrict__ rope,
-                                          int64_t kv0, int kt, int kv_hi, int64_t N_kv, int wave, int lane) {
-    constexpr int LV = S::LAT_VECS + 1, RV = S::ROPE_VECS + 1;
-    const int lk = DL * 2 == 1024 ? 0 : lane / LV;            // row of the load this lane fills
-    const int lc = DL * 2 == 1024 ? lane : lane - lk * LV;    // 16-byte chunk inside that row
-    const bool lon = DL * 2 == 1024 || (lc < S::LAT_VECS && lk < S::LAT_ROWS_PER_LOAD);
+// Wide shape, latent load i (0..15) of this wave for KV tile kt: row n = 4 i + wave of
+// the tile, one 1024-byte row per load. Keys past the tile's extent are clamped to the
+// last valid row (finite values; their scores are masked).
+template <class T, int DL>
+__device__ __forceinline__ void wide_lat_load(char* dst, const char* __restrict__ lat, int64_t kv0, int kt,
+                                              int64_t last, int wave, int lane, int i) {
+    const int n = i * 4 + wave;
+    const int64_t j = min((int64_t)kt * BN + n, last);
+    lds_dma16(lat + (kv0 + j) * (DL * 2) + lane * 16, dst + n * T::LAT_STRIDE);
+}
+
+// Wide shape, rope load u (0..1) of this wave: rows 8 n .. 8 n + 7 with n = 2 wave + u.
+// Lane l fills LDS chunk l % 8 of row 8 n + l / 8, i.e. source chunk (l % 8) ^ ((row/2) % 8).
+template <class T, int DR>
+__device__ __forceinline__ void wide_rope_load(char* dst, const char* __restrict__ rope, int64_t kv0, int kt,
+                                               int64_t last, int wave, int lane, int u) {
+    const int n = 2 * wave + u;
+    const int r = n * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int64_t j = min((int64_t)kt * BN + r, last);
+    lds_dma16(rope + (kv0 + j) * (DR * 2) + c * 16, dst + T::ROPE_OFF + n * 1024);
+}
+
+// Other shapes: every load of tile kt, lanes that would land on a pad switched off.
+// Wave w issues loads w, w+4, ...
+template <class T, int DL, int DR>
+__device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restrict__ lat,
+                                                 const char* __restrict__ rope, int64_t kv0, int kt,
+                                                 int64_t last, int wave, int lane) {
+    constexpr int LV = T::LAT_VECS + 1, RV = T::ROPE_VECS + 1;
+    const int lk = lane / LV;
+    const int lc = lane - lk * LV;
+    const bool lon = lc < T::LAT_VECS && lk < T::LAT_ROWS_PER_LOAD;
     const int rk = lane / RV;
     const int rc = lane - rk * RV;
-    const bool ron = rc < S::ROPE_VECS && rk < S::ROPE_ROWS_PER_LOAD;
-    const int64_t last = min((int64_t)kv_hi - 1, N_kv - 1 - kv0);
+    const bool ron = rc < T::ROPE_VECS && rk < T::ROPE_ROWS_PER_LOAD;
 #pragma unroll
-    for (int i = 0; i < (S::LAT_LOADS + 3) / 4; ++i) {
+    for (int i = 0; i < (T::LAT_LOADS + 3) / 4; ++i) {
         const int n = i * 4 + wave;
-        if (n >= S::LAT_LOADS) break;
-        const int r = n * S::LAT_ROWS_PER_LOAD + lk;
+        if (n >= T::LAT_LOADS) break;
+        const int r = n * T::LAT_ROWS_PER_LOAD + lk;
         const int64_t j = min((int64_t)kt * BN + r, last);
         if (lon && r < BN)
-            lds_dma16(lat + (kv0 + j) * (DL * 2) + lc * 16, dst + n * S::LAT_ROWS_PER_LOAD * S::LAT_STRIDE);
+            lds_dma16(lat + (kv0 + j) * (DL * 2) + lc * 16, dst + n * T::LAT_ROWS_PER_LOAD * T::LAT_STRIDE);
     }
 #pragma unroll
-    for (int i = 0; i < (S::ROPE_LOADS + 3) / 4; ++i) {
+    for (int i = 0; i < (T::ROPE_LOADS + 3) / 4; ++i) {
         const int n = i * 4 + ((wave + 2) & 3);
-        if (n >= S::ROPE_LOADS) break;
-        const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
+        if (n >= T::ROPE_LOADS) break;
+        const int r = n * T::ROPE_ROWS_PER_LOAD + rk;
         const int64_t j = min((int64_t)kt * BN + r, last);
         if (ron && r < BN)
             lds_dma16(rope + (kv0 + j) * (DR * 2) + rc * 16,
-                      dst + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
+                      dst + T::ROPE_OFF + n * T::ROPE_ROWS_PER_LOAD * T::ROPE_STRIDE);
     }
 }
 
@@ -128,12 +187,14 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
-    using S = Shape<DL, DR>;
-    __shared__ __attribute__((aligned(1024))) char kv_lds0[S::TILE_BYTES];  // KV tile double buffer:
-    __shared__ __attribute__((aligned(1024))) char kv_lds1[S::TILE_BYTES];  // two separate objects
-    __shared__ Exchange ex;
-    __shared__ int sh[NT];
+    using T = DenseTile<DL, DR>;
+    __shared__ __attribute__((aligned(1024))) char kv_lds0[T::TILE_BYTES];  // KV tile double buffer:
+    __shared__ __attribute__((aligned(1024))) char kv_lds1[T::TILE_BYTES];  // two separate objects
+    __shared__ __attribute__((aligned(16))) uint4 Px[NT / 64][2][64];  // P fragment exchange
+    __shared__ float mx[NT / 64][64];                                  // tile maxima / row sums
+    __shared__ int flag[NT / 64];
     __shared__ int s_maxpos[NT / 64];
+    int* sh = reinterpret_cast<int*>(&Px[0][0][0]);  // scan scratch, used before the KV loop only
 
     int v, tile;
     find_tile((int)blockIdx.x, cu, n_vrows, H, sh, v, tile);
@@ -142,7 +203,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     if (v < 0) return;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1;
     const int side = wave & 1;    // keys [32 side, +32) of each tile; O columns [DL/2 side, +DL/2)
     const int lane = tid & 63;
@@ -164,11 +225,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     if (lane == 0) s_maxpos[wave] = mp;
 
     // Q^T fragments: lane holds row l32, elements [16 kb + 8 half, +8) of every k-block.
-    bf16x8 qf[S::KB];
+    bf16x8 qf[T::KB];
     {
-        const __bf16* qrow = q + grow * S::DQK + 8 * half;
+        const __bf16* qrow = q + grow * T::DQK + 8 * half;
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb)
+        for (int kb = 0; kb < T::KB; ++kb)
             qf[kb] = valid ? *reinterpret_cast<const bf16x8*>(qrow + kb * 16) : bf16x8{};
     }
     __syncthreads();
@@ -181,44 +242,211 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) pmin = min(pmin, __shfl_xor(pmin, off));
     pmin = __builtin_amdgcn_readfirstlane(pmin);
+    const int64_t last = min((int64_t)kv_hi - 1, N_kv - 1 - kv0);  // last key row that may be read
 
-    constexpr int NB0 = S::NB / 2;  // O column blocks per wave
+    constexpr int NB0 = T::NB / 2;  // O column blocks per wave
     f32x16 acc_o[NB0];
 #pragma unroll
     for (int d = 0; d < NB0; ++d) acc_o[d] = f32x16{};
     float m_ref = -INFINITY;  // lazy reference max (log2 domain) of this lane's row
     float l_run = 0.0f;       // running sum over this lane's share of the keys
 
-    const LaneOffsets<S> lo(side, lane);
+    // Per-lane LDS offsets inside a tile (everything else is an immediate):
+    //  * Q K^T reads: LDS row of score row l32, 8 elements at 8*half of each k-block;
+    //  * V^T reads: LDS row of score row 4*half + (lane%16)/4 of a 16-key block, dims
+    //    16*((lane/16)%2) + 4*(lane%4); the second read of an MFMA is 2 rows further.
+    const int krow = 32 * side + 16 * (l32 >> 4) + kperm(l32 & 15);
+    const int k_lat_off = krow * T::LAT_STRIDE + 16 * half;
+    int k_rope_off[T::KB - DL / 16];
+#pragma unroll
+    for (int kb = 0; kb < T::KB - DL / 16; ++kb) {
+        if constexpr (T::WIDE)
+            k_rope_off[kb] = T::ROPE_OFF + krow * T::ROPE_STRIDE + 16 * ((2 * kb + half) ^ ((krow >> 1) & 7));
+        else
+            k_rope_off[kb] = T::ROPE_OFF + krow * T::ROPE_STRIDE + 16 * half + 32 * kb;
+    }
+    const int v_off = kperm(4 * half + ((lane & 15) >> 2)) * T::LAT_STRIDE + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+
     const int n_tiles = (kv_hi + BN - 1) / BN;
 
-    // One KV tile: wait for it, publish it, start streaming the next tile into the other
-    // buffer, then scores, softmax, P exchange and P V on this one. The two buffers are
-    // distinct LDS objects, so the compiler can tell that the streaming loads never
-    // touch the tile being read and does not wait for them.
+    // One KV tile: wait for it, publish it, then scores, softmax, P exchange and P V on
+    // it while the next tile streams into the other buffer. The two buffers are distinct
+    // LDS objects, so the compiler can tell that the streaming loads never touch the tile
+    // being read and does not wait for them. The wide shape issues the next tile's loads
+    // unconditionally (clamped rows; after the last tile they refill an unused buffer).
     auto tile_step = [&](const char* kvt, char* nxt, int kt) {
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
+        for (int kb = 0; kb < T::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
         __syncthreads();                     // ... and every wave's; the other buffer is free
-        if (kt + 1 < n_tiles) load_tile<S, DL, DR>(nxt, lat, rope, kv0, kt + 1, kv_hi, N_kv, wave, lane);
-        const int key0 = kt * BN + 32 * side + 4 * half;  // key of s[0]
-        auto causal = [&](f32x16& s) {
-            if (kt * BN + 32 * side + 31 > pmin) {  // wave-uniform: a causal diagonal crosses these keys
+        if constexpr (!T::WIDE) {
+            if (kt + 1 < n_tiles) narrow_load_tile<T, DL, DR>(nxt, lat, rope, kv0, kt + 1, last, wave, lane);
+        }
+        // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
+        f32x16 s = f32x16{};
+        {
+            const char* kl = kvt + k_lat_off;
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (T::WIDE) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] = key0 + 8 * (i >> 2) + (i & 3) <= pos ? s[i] : -INFINITY;
+                for (int i = 0; i < T::LAT_PER_WAVE; ++i) wide_lat_load<T, DL>(nxt, lat, kv0, kt + 1, last, wave, lane, i);
+#pragma unroll
+                for (int u = 0; u < T::ROPE_PER_WAVE; ++u) wide_rope_load<T, DR>(nxt, rope, kv0, kt + 1, last, wave, lane, u);
             }
-        };
-        tile_compute<S, DL>(kvt, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex, causal, [] {});
+#pragma unroll
+            for (int kb = 0; kb < T::KB; ++kb) {
+                const char* ap = kb < DL / 16 ? kl + kb * 32 : kvt + k_rope_off[kb - DL / 16];
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
+            }
+            // QK_AHEAD operand reads in flight ahead of the MFMA chain; a load of the next
+            // tile after every LOAD_GAP-th MFMA, so the vector memory pipe drains them
+            // while the matrix core runs instead of stalling the wave on a burst.
+            constexpr int AHEAD = T::KB < QK_AHEAD ? T::KB : QK_AHEAD;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int kb = 0; kb < T::KB - AHEAD; ++kb) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (T::WIDE && kb % T::LOAD_GAP == 0 && kb / T::LOAD_GAP < T::LOADS_PER_WAVE)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt * BN + 32 * side + 31 > pmin) {  // wave-uniform: a causal diagonal crosses these keys
+            const int rel = pos - kt * BN;      // keys of this tile up to rel are visible
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = score_key(side, half, i) <= rel ? s[i] : -INFINITY;
+        }
+        float smax = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) smax = fmaxf(smax, s[i]);
+        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        const float mloc = smax * scale_log2;  // max over this wave's 32 keys (log2 units)
+        // Fast path: P against the current reference, published with a "needs a new
+        // reference" flag; the slow path (any wave flagged) agrees on the pair max first.
+        const bool need = mloc > m_ref + kRescale;
+        float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+        float pf[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -m_use));
+        bf16x8 pk[2];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pk[0][j] = (__bf16)pf[j];
+            pk[1][j] = (__bf16)pf[8 + j];
+        }
+        Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
+        Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
+        mx[wave][lane] = mloc;
+        const bool any_need = __ballot(need) != 0;
+        if (lane == 0) flag[wave] = any_need;
+        __syncthreads();
+        int slow = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) slow |= flag[w];
+        if (slow) {  // workgroup-uniform
+            const float m_pair = fmaxf(mloc, mx[wave ^ 1][lane]);
+            const bool bump = m_pair > m_ref + kRescale;
+            const float m_new = bump ? m_pair : m_ref;
+            m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_ref - m_use) : 1.0f;
+            l_run *= alpha;
+            m_ref = m_new;
+#pragma unroll
+            for (int d = 0; d < NB0; ++d) acc_o[d] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) pf[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], scale_log2, -m_use));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                pk[0][j] = (__bf16)pf[j];
+                pk[1][j] = (__bf16)pf[8 + j];
+            }
+            __syncthreads();  // everyone has read the flags and the fast-path P
+            Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
+            Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
+            __syncthreads();
+        }
+        float lsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum += pf[i];
+        l_run += lsum;
+        // P^T fragments: our two key blocks (tile rows 32*side + [0,32)) and the partner's
+        // (rows 32*(1-side) + [0,32)); the matching V rows are picked by address.
+        const bf16x8 po0 = __builtin_bit_cast(bf16x8, Px[wave ^ 1][0][lane]);
+        const bf16x8 po1 = __builtin_bit_cast(bf16x8, Px[wave ^ 1][1][lane]);
+
+        // O^T[dim, row] += V^T[dim, key] P^T[key, row] over this wave's column blocks.
+        // Element j of the lane's k-slice of a 16-key block is key
+        // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
+        __builtin_amdgcn_sched_barrier(0);
+        const char* v_own = kvt + v_off + (32 * side) * T::LAT_STRIDE;
+        const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
+#pragma unroll
+        for (int d = 0; d < NB0; ++d) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * T::LAT_STRIDE));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
+                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);
+            }
+        }
+        {
+            // two transposing reads per MFMA, PV_AHEAD MFMAs' worth of reads in flight
+            constexpr int NM = NB0 * 4;
+            constexpr int AHEAD = NM < PV_AHEAD ? NM : PV_AHEAD;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+            for (int m = 0; m < NM - AHEAD; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
-    load_tile<S, DL, DR>(kv_lds0, lat, rope, kv0, 0, kv_hi, N_kv, wave, lane);
+    if constexpr (T::WIDE) {
+#pragma unroll
+        for (int i = 0; i < T::LAT_PER_WAVE; ++i) wide_lat_load<T, DL>(kv_lds0, lat, kv0, 0, last, wave, lane, i);
+#pragma unroll
+        for (int u = 0; u < T::ROPE_PER_WAVE; ++u) wide_rope_load<T, DR>(kv_lds0, rope, kv0, 0, last, wave, lane, u);
+    } else {
+        narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, kv0, 0, last, wave, lane);
+    }
     for (int kt = 0; kt < n_tiles; kt += 2) {
         tile_step(kv_lds0, kv_lds1, kt);
         if (kt + 1 >= n_tiles) break;
         tile_step(kv_lds1, kv_lds0, kt + 1);
     }
-    write_rows<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, o_out, lse_out);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // loads issued after the last tile landed before LDS is released
+
+    // Row sums: this lane's share + the other half-wave's + the partner wave's.
+    float l_w = l_run + __shfl_xor(l_run, 32);
+    __syncthreads();
+    mx[wave][lane] = l_w;
+    __syncthreads();
+    const float l_tot = l_w + mx[wave ^ 1][lane];
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (valid) {
+        __bf16* orow = o_out + grow * DL;
+#pragma unroll
+        for (int d = 0; d < NB0; ++d) {
+            const int db = side * NB0 + d;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc_o[d][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * g + 4 * half) = y;
+            }
+        }
+        if (side == 0 && half == 0) lse_out[grow] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
 }
 
 template <int DL, int DR>
@@ -237,6 +465,5 @@ hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream) {
     if (a.D_latent == 512) return launch_dense<512, 64>(a, stream);
     return launch_dense<64, 16>(a, stream);
 }
-
 
 }  // namespace mla

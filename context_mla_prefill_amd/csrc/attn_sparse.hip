@@ -198,10 +198,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         const int tn = next_live(t + 1);
         if (tn < n_tiles) gather_latent(tn, ms ^ 1);
         auto keymask = [&](f32x16& s) {
-            const int key0 = 32 * side + 4 * half;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                s[i] = (bits >> (key0 + 8 * (i >> 2) + (i & 3))) & 1 ? s[i] : -INFINITY;
+            for (int i = 0; i < 16; ++i) s[i] = (bits >> score_key(side, half, i)) & 1 ? s[i] : -INFINITY;
         };
         auto rope_next = [&] {
             if (tn < n_tiles) gather_rope(tn);

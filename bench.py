@@ -60,6 +60,10 @@ def merge_bytes(merge_src: np.ndarray, H: int, Dv: int) -> float:
     return float(n_contrib * H * (2 * Dv + 4) + T * H * (2 * Dv + 4) + T * P * 4)
 
 
+# sources the dense attention kernel is compiled from (its traffic record names their hash)
+ATTN_SOURCES = ("attn_dense.hip", "attn_core.h")
+
+
 def measured_traffic(workload: int):
     """HBM bytes per launch of the attention and merge kernels from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy kernel), or None when the kernel
@@ -70,11 +74,14 @@ def measured_traffic(workload: int):
         return None, None
     rec = json.load(open(path))
 
-    def sha(name):
-        with open(os.path.join(ROOT, "context_mla_prefill_amd", "csrc", name), "rb") as f:
-            return hashlib.sha256(f.read()).hexdigest()[:16]
+    def sha(*names):
+        h = hashlib.sha256()
+        for name in names:
+            with open(os.path.join(ROOT, "context_mla_prefill_amd", "csrc", name), "rb") as f:
+                h.update(f.read())
+        return h.hexdigest()[:16]
 
-    att = rec["bytes_per_launch"] if sha("attn_dense.hip") == rec["kernel_source_sha256_prefix"] else None
+    att = rec["bytes_per_launch"] if sha(*ATTN_SOURCES) == rec["kernel_source_sha256_prefix"] else None
     mer = rec["merge_bytes_per_launch"] if sha("merge.hip") == rec["merge_source_sha256_prefix"] else None
     return att, mer
 

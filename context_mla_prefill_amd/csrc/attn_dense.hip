@@ -124,28 +124,43 @@ __device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ 
     tile_out = s_tile;
 }
 
-// Wide shape, latent load i (0..15) of this wave for KV tile kt: row n = 4 i + wave of
-// the tile, one 1024-byte row per load. Keys past the tile's extent are clamped to the
-// last valid row (finite values; their scores are masked).
-template <class T, int DL>
-__device__ __forceinline__ void wide_lat_load(char* dst, const char* __restrict__ lat, int64_t kv0, int kt,
-                                              int64_t last, int wave, int lane, int i) {
-    const int n = i * 4 + wave;
-    const int64_t j = min((int64_t)kt * BN + n, last);
-    lds_dma16(lat + (kv0 + j) * (DL * 2) + lane * 16, dst + n * T::LAT_STRIDE);
-}
+// Buffer-resource flags (gfx9 raw buffer: 32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
-// Wide shape, rope load u (0..1) of this wave: rows 8 n .. 8 n + 7 with n = 2 wave + u.
-// Lane l fills LDS chunk l % 8 of row 8 n + l / 8, i.e. source chunk (l % 8) ^ ((row/2) % 8).
-template <class T, int DR>
-__device__ __forceinline__ void wide_rope_load(char* dst, const char* __restrict__ rope, int64_t kv0, int kt,
-                                               int64_t last, int wave, int lane, int u) {
-    const int n = 2 * wave + u;
-    const int r = n * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int64_t j = min((int64_t)kt * BN + r, last);
-    lds_dma16(rope + (kv0 + j) * (DR * 2) + c * 16, dst + T::ROPE_OFF + n * 1024);
-}
+// Wide shape: buffer views of the rows of KV tile kt. The base is the tile's first row,
+// clamped to the last valid row (the loads issued after the final tile read that row into
+// the unused buffer); the range is the valid rows from the base, so a load can only touch
+// rows of this request's extent. Buffer loads rather than global ones: the compiler counts
+// a global (flat-family) load into LDS as an LDS access of unknown order and would then
+// wait for all LDS reads at once instead of keeping the Q K^T reads in flight.
+template <class T, int DL, int DR>
+struct WideTile {
+    __amdgpu_buffer_rsrc_t lat_rsrc, rope_rsrc;
+    int rows;  // valid rows from the base, 1..BN
+    __device__ __forceinline__ WideTile(const char* lat, const char* rope, int64_t kv0, int kt, int64_t last) {
+        const int64_t tb = min((int64_t)kt * BN, last);
+        rows = (int)min((int64_t)BN, last - tb + 1);
+        lat_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(lat + (kv0 + tb) * (DL * 2)), 0, rows * (DL * 2), kBufferFlags);
+        rope_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rope + (kv0 + tb) * (DR * 2)), 0, rows * (DR * 2), kBufferFlags);
+    }
+    // Latent load i (0..15) of this wave: tile row n = 4 i + wave, one 1024-byte row per
+    // load (row offset in an SGPR, lane offset constant). Rows past the extent repeat the
+    // last valid row (finite values; their scores are masked).
+    __device__ __forceinline__ void lat_load(char* dst, int wave, int lane, int i) const {
+        const int n = i * 4 + wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(dst + n * T::LAT_STRIDE), 16, lane * 16,
+                                                 min(n, rows - 1) * (DL * 2), 0, 0);
+    }
+    // Rope load u (0..1) of this wave: rows 8 n .. 8 n + 7 with n = 2 wave + u. Lane l fills
+    // LDS chunk l % 8 of row 8 n + l / 8, i.e. source chunk (l % 8) ^ ((row / 2) % 8).
+    __device__ __forceinline__ void rope_load(char* dst, int wave, int lane, int u) const {
+        const int n = 2 * wave + u;
+        const int r = n * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rsrc, (lds_void*)(dst + T::ROPE_OFF + n * 1024), 16,
+                                                 min(r, rows - 1) * (DR * 2) + c * 16, 0, 0, 0);
+    }
+};
 
 // Other shapes: every load of tile kt, lanes that would land on a pad switched off.
 // Wave w issues loads w, w+4, ...
@@ -179,6 +194,12 @@ __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restri
             lds_dma16(rope + (kv0 + j) * (DR * 2) + rc * 16,
                       dst + T::ROPE_OFF + n * T::ROPE_ROWS_PER_LOAD * T::ROPE_STRIDE);
     }
+}
+
+// Value of x in lane l ^ 32: one VALU lane swap of the two half-waves, no LDS round trip.
+__device__ __forceinline__ float half_swap(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    return __builtin_bit_cast(float, (int)((__lane_id() < 32) ? r[1] : r[0]));
 }
 
 template <int DL, int DR>
@@ -288,10 +309,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
             const char* kl = kvt + k_lat_off;
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (T::WIDE) {
+                const WideTile<T, DL, DR> src(lat, rope, kv0, kt + 1, last);
 #pragma unroll
-                for (int i = 0; i < T::LAT_PER_WAVE; ++i) wide_lat_load<T, DL>(nxt, lat, kv0, kt + 1, last, wave, lane, i);
+                for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(nxt, wave, lane, i);
 #pragma unroll
-                for (int u = 0; u < T::ROPE_PER_WAVE; ++u) wide_rope_load<T, DR>(nxt, rope, kv0, kt + 1, last, wave, lane, u);
+                for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(nxt, wave, lane, u);
             }
 #pragma unroll
             for (int kb = 0; kb < T::KB; ++kb) {
@@ -322,7 +344,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         float smax = s[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) smax = fmaxf(smax, s[i]);
-        smax = fmaxf(smax, __shfl_xor(smax, 32));
+        smax = fmaxf(smax, half_swap(smax));
         const float mloc = smax * scale_log2;  // max over this wave's 32 keys (log2 units)
         // Fast path: P against the current reference, published with a "needs a new
         // reference" flag; the slow path (any wave flagged) agrees on the pair max first.
@@ -379,14 +401,15 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 
         // O^T[dim, row] += V^T[dim, key] P^T[key, row] over this wave's column blocks.
         // Element j of the lane's k-slice of a 16-key block is key
-        // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
+        // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each. Key-block
+        // major: the own key blocks first, so the partner's P has 16 MFMAs to arrive.
         __builtin_amdgcn_sched_barrier(0);
         const char* v_own = kvt + v_off + (32 * side) * T::LAT_STRIDE;
         const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
 #pragma unroll
-        for (int d = 0; d < NB0; ++d) {
+        for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int d = 0; d < NB0; ++d) {
                 const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * T::LAT_STRIDE));
@@ -411,10 +434,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     };
 
     if constexpr (T::WIDE) {
+        const WideTile<T, DL, DR> src(lat, rope, kv0, 0, last);
 #pragma unroll
-        for (int i = 0; i < T::LAT_PER_WAVE; ++i) wide_lat_load<T, DL>(kv_lds0, lat, kv0, 0, last, wave, lane, i);
+        for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(kv_lds0, wave, lane, i);
 #pragma unroll
-        for (int u = 0; u < T::ROPE_PER_WAVE; ++u) wide_rope_load<T, DR>(kv_lds0, rope, kv0, 0, last, wave, lane, u);
+        for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(kv_lds0, wave, lane, u);
     } else {
         narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, kv0, 0, last, wave, lane);
     }

@@ -14,9 +14,10 @@
 //    Q of those rows in registers for the whole KV loop.
 //  * KV tiles of BN = 64 keys move HBM -> LDS with direct-to-LDS loads into a double
 //    buffer (the next tile streams in while the current one is used) and are shared by
-//    all heads and waves. For the 512+64 shape the loads of the next tile are spread
-//    over the Q K^T MFMAs of the current one (two MFMAs apart), so the CU's vector
-//    memory pipe drains them while the matrix core runs instead of stalling the wave.
+//    all heads and waves. For the 512+64 shape the latent loads of the next tile are
+//    spread over the Q K^T MFMAs of the current one (two MFMAs apart), so the CU's
+//    vector memory pipe drains them while the matrix core runs instead of stalling the
+//    wave, and the barrier that publishes P orders LDS only, leaving them in flight.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, A = K from
 //    LDS, B = Q^T from registers); wave s of a pair scores keys [32 s, 32 s + 32) of the
 //    tile. Each lane then holds scores of ONE query row, so the row max needs one
@@ -64,12 +65,11 @@ struct DenseTile {
     static constexpr int ROPE_ROWS_PER_LOAD = WIDE ? 8 : 64 / (ROPE_VECS + 1);
     static constexpr int LAT_LOADS = (BN + LAT_ROWS_PER_LOAD - 1) / LAT_ROWS_PER_LOAD;
     static constexpr int ROPE_LOADS = (BN + ROPE_ROWS_PER_LOAD - 1) / ROPE_ROWS_PER_LOAD;
-    // wide shape: every wave issues LAT_PER_WAVE latent and ROPE_PER_WAVE rope loads of
-    // the next tile, one after every LOAD_GAP-th Q K^T MFMA (the last few, which find
-    // no slot there, go among the final MFMAs of the chain)
+    // wide shape: every wave issues LAT_PER_WAVE latent loads of the next tile, one after
+    // every LOAD_GAP-th Q K^T MFMA (the last few, which find no slot there, go among the
+    // final MFMAs of the chain), and its ROPE_PER_WAVE rope loads right after the chain
     static constexpr int LAT_PER_WAVE = LAT_LOADS / 4;    // 16
     static constexpr int ROPE_PER_WAVE = ROPE_LOADS / 4;  // 2
-    static constexpr int LOADS_PER_WAVE = LAT_PER_WAVE + ROPE_PER_WAVE;
     static constexpr int LOAD_GAP = 2;
     static_assert(DQK % 16 == 0 && DL % 32 == 0 && DR % 8 == 0, "tile shape");
     static_assert(!WIDE || (LAT_LOADS % 4 == 0 && ROPE_LOADS % 4 == 0), "wide loads split evenly over 4 waves");
@@ -196,6 +196,11 @@ __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restri
     }
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations but not for
+// its buffer loads into LDS, so the next tile's loads stay in flight across it (a full
+// __syncthreads() also waits for every outstanding vector-memory load).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Value of x in lane l ^ 32: one VALU lane swap of the two half-waves, no LDS round trip.
 __device__ __forceinline__ float half_swap(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
@@ -312,8 +317,6 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
                 const WideTile<T, DL, DR> src(lat, rope, kv0, kt + 1, last);
 #pragma unroll
                 for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(nxt, wave, lane, i);
-#pragma unroll
-                for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(nxt, wave, lane, u);
             }
 #pragma unroll
             for (int kb = 0; kb < T::KB; ++kb) {
@@ -330,12 +333,33 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
             for (int kb = 0; kb < T::KB - AHEAD; ++kb) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (T::WIDE && kb % T::LOAD_GAP == 0 && kb / T::LOAD_GAP < T::LOADS_PER_WAVE)
+                if (T::WIDE && kb % T::LOAD_GAP == 0 && kb / T::LOAD_GAP < T::LAT_PER_WAVE)
                     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (T::WIDE) {
+            const WideTile<T, DL, DR> src(lat, rope, kv0, kt + 1, last);
+#pragma unroll
+            for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(nxt, wave, lane, u);
+        }
+        // V^T operands of the first P V MFMAs (key-block-major: kb = m / NB0, d = m % NB0):
+        // they do not depend on P, so their LDS reads run under the softmax.
+        constexpr int NM = NB0 * 4;
+        constexpr int PA = NM < PV_AHEAD ? NM : PV_AHEAD;
+        constexpr int NVB = PA + 1;
+        const char* v_own = kvt + v_off + (32 * side) * T::LAT_STRIDE;
+        const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
+        s16x4 vlo[NVB], vhi[NVB];
+        auto vread = [&](int m) {
+            const int kb = m / NB0, d = m % NB0;
+            const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
+            vlo[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+            vhi[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * T::LAT_STRIDE));
+        };
+#pragma unroll
+        for (int m = 0; m < PA; ++m) vread(m);
         if (kt * BN + 32 * side + 31 > pmin) {  // wave-uniform: a causal diagonal crosses these keys
             const int rel = pos - kt * BN;      // keys of this tile up to rel are visible
 #pragma unroll
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         mx[wave][lane] = mloc;
         const bool any_need = __ballot(need) != 0;
         if (lane == 0) flag[wave] = any_need;
-        __syncthreads();
+        lds_barrier();
         int slow = 0;
 #pragma unroll
         for (int w = 0; w < NT / 64; ++w) slow |= flag[w];
@@ -404,31 +428,13 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each. Key-block
         // major: the own key blocks first, so the partner's P has 16 MFMAs to arrive.
         __builtin_amdgcn_sched_barrier(0);
-        const char* v_own = kvt + v_off + (32 * side) * T::LAT_STRIDE;
-        const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-            for (int d = 0; d < NB0; ++d) {
-                const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * T::LAT_STRIDE));
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
-                acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);
-            }
-        }
-        {
-            // two transposing reads per MFMA, PV_AHEAD MFMAs' worth of reads in flight
-            constexpr int NM = NB0 * 4;
-            constexpr int AHEAD = NM < PV_AHEAD ? NM : PV_AHEAD;
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
-#pragma unroll
-            for (int m = 0; m < NM - AHEAD; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+        for (int m = 0; m < NM; ++m) {  // PA MFMAs' worth of V^T reads in flight
+            const int kb = m / NB0, d = m % NB0;
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[m % NVB], vhi[m % NVB], 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
+            acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);
+            if (m + PA < NM) vread(m + PA);
             __builtin_amdgcn_sched_barrier(0);
         }
     };

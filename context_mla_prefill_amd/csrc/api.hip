@@ -120,6 +120,9 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
     return MLA_OK;
 }
 
+// The sparse kernel addresses KV rows through 32-bit buffer offsets: N_kv * 512 < 2^32.
+constexpr int64_t kSparseMaxKv = (int64_t(1) << 23) - 1;
+
 mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
     if (!a) return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: null args");
     if (a->T_loc < 0 || a->n_vrows < 0 || a->N_kv < 0 || a->N_kv > INT32_MAX)
@@ -146,6 +149,9 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
         if (!big || a->kv_dtype != MLA_KV_FP8_E4M3 || a->H % 64 != 0)
             return fail(MLA_ERR_UNSUPPORTED,
                         "mla_prefill_partial: sparse path needs 512+64 dims, fp8 KV and H %% 64 == 0");
+        if (a->N_kv > kSparseMaxKv)
+            return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path takes at most %d KV rows",
+                        (int)kSparseMaxKv);
     } else if (a->kv_dtype != MLA_KV_BF16) {
         return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: dense path takes bf16 KV");
     }

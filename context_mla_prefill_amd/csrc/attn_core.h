@@ -58,6 +58,22 @@ __device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
     __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Buffer-resource flags (gfx9 raw buffer: 32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
+
+// Direct-to-LDS buffer load: lane l copies 16 bytes from byte offset voff of the buffer to
+// LDS address lds_base + 16*l. Buffer (not global) loads: the compiler counts a global
+// (flat-family) load into LDS as an LDS access of unknown order and then waits for every
+// LDS read at once instead of keeping operand reads in flight.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, char* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations but not for
+// its loads into LDS, which stay in flight across it (__syncthreads() also waits for every
+// outstanding vector-memory load).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // LDS the two waves of a pair exchange through.
 struct Exchange {
     uint4 Px[NT / 64][2][64];  // bf16 P fragments
@@ -152,7 +168,7 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
     ex.mx[wave][lane] = mloc;
     const bool any_need = __ballot(need) != 0;
     if (lane == 0) ex.flag[wave] = any_need;
-    __syncthreads();
+    lds_barrier();
     after_exchange();
     int slow = 0;
 #pragma unroll

@@ -124,9 +124,6 @@ __device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ 
     tile_out = s_tile;
 }
 
-// Buffer-resource flags (gfx9 raw buffer: 32-bit data format, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
-
 // Wide shape: buffer views of the rows of KV tile kt. The base is the tile's first row,
 // clamped to the last valid row (the loads issued after the final tile read that row into
 // the unused buffer); the range is the valid rows from the base, so a load can only touch
@@ -195,11 +192,6 @@ __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restri
                       dst + T::ROPE_OFF + n * T::ROPE_ROWS_PER_LOAD * T::ROPE_STRIDE);
     }
 }
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS operations but not for
-// its buffer loads into LDS, so the next tile's loads stay in flight across it (a full
-// __syncthreads() also waits for every outstanding vector-memory load).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Value of x in lane l ^ 32: one VALU lane swap of the two half-waves, no LDS round trip.
 __device__ __forceinline__ float half_swap(float x) {

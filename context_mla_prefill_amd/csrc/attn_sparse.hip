@@ -70,7 +70,13 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const int p = positions[tok];
     const int head = hg * BM + pair * 32 + l32;
     const int64_t grow = (int64_t)tok * H + head;
-    const int64_t last_row = N_kv - 1;
+    // Buffer views of this request's KV rows (keys are request-relative): fp8 latent rows of
+    // DL bytes and bf16 rope rows. The caller keeps N_kv * DL below 2^32.
+    const int last_key = (int)(N_kv - 1 - kv0);
+    const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(lat8 + kv0 * DL), 0, (int)(uint32_t)((N_kv - kv0) * DL), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(rope + kv0 * (DR * 2)), 0, (int)(uint32_t)((N_kv - kv0) * (DR * 2)), kBufferFlags);
 
     for (int i = tid; i < MAX_TOPK; i += NT) sel[i] = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
 
@@ -115,12 +121,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
             const int n = i * 4 + wave;
             const int j = 2 * n + half;
             bool ok;
-            const int64_t row = min(kv0 + slot_key(t, j, ok), last_row);
-            lds_dma16(lat8 + row * DL + l32 * 16, (char*)stage + n * 1024);
+            const int key = min(slot_key(t, j, ok), last_key);
+            lds_dma16(lat_rsrc, (uint32_t)key * DL + l32 * 16, (char*)stage + n * 1024);
         }
         if (wave == 0) {
             bool ok;
-            const int64_t row = min(kv0 + slot_key(t, lane, ok), last_row);
+            const int64_t row = kv0 + min(slot_key(t, lane, ok), last_key);
             stage_scale[lane] = kv_scale[row >> 6];
             const uint64_t bits = __ballot(ok);
             if (lane == 0) tmask[mslot] = bits;
@@ -138,9 +144,10 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
             if (n >= S::ROPE_LOADS) break;  // wave-uniform
             const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
             bool ok;
-            const int64_t row = min(kv0 + slot_key(t, r < BN ? r : 0, ok), last_row);
+            const int key = min(slot_key(t, r < BN ? r : 0, ok), last_key);
             if (ron && r < BN)
-                lds_dma16(rope + row * (DR * 2) + rc * 16, kv_tile + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
+                lds_dma16(rope_rsrc, (uint32_t)key * (DR * 2) + rc * 16,
+                          kv_tile + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
         }
     };
     // Dequantises the staged fp8 rows into the bf16 tile: thread handles 16-byte chunks

@@ -167,7 +167,8 @@ typedef struct mla_partial_args {
 
 /* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales);
  * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
- * bf16 KV or with H not a multiple of 64, dense with fp8 KV, dtype); HIP.
+ * bf16 KV, with H not a multiple of 64 or with N_kv >= 2^23 rows, dense with fp8 KV,
+ * dtype); HIP.
  * Sparse preconditions: selected indices of a row are distinct; entries outside [0, p]
  * (including -1) are pads. */
 mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);

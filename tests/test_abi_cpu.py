@@ -106,6 +106,8 @@ def test_partial_validation_errors():
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64))[0] == _lib.MLA_ERR_UNSUPPORTED  # bf16 sparse
     assert call(_args(**ok, topk_idx=f, topk=64, window=5000, kv_dtype=1, kv_scale=f, H=64))[0] == \
         _lib.MLA_ERR_UNSUPPORTED
+    assert call(_args(**ok, topk_idx=f, topk=64, window=128, kv_dtype=1, kv_scale=f, H=64, N_kv=1 << 23))[0] == \
+        _lib.MLA_ERR_UNSUPPORTED  # sparse KV rows addressed by 32-bit byte offsets
     st, msg = call(_args(**ok, D_rope=32))
     assert st == _lib.MLA_ERR_UNSUPPORTED and "dims" in msg
     # empty shard: nothing to do, OK without touching any pointer

@@ -74,6 +74,12 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // outstanding vector-memory load).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Value of x in lane l ^ 32: one VALU lane swap of the two half-waves, no LDS round trip.
+__device__ __forceinline__ float half_swap(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    return __builtin_bit_cast(float, (int)((__lane_id() < 32) ? r[1] : r[0]));
+}
+
 // LDS the two waves of a pair exchange through.
 struct Exchange {
     uint4 Px[NT / 64][2][64];  // bf16 P fragments
@@ -95,7 +101,8 @@ __device__ __forceinline__ int score_key(int side, int half, int i) {
 }
 
 // Per-lane LDS offsets inside a tile (everything else is an immediate):
-//  * Q K^T reads: LDS row of score row l32, 8 elements at 8*half of each 16-wide k-block;
+//  * Q K^T reads: LDS row of score row l32, 8 elements at 8*half of each 16-wide k-block
+//    (latent offsets from the latent rows' base, rope offsets from the rope rows' base);
 //  * V^T reads (first of the two per MFMA): LDS row of score row 4*half + (lane%16)/4 of
 //    the key block, dims 16*((lane/16)%2) + 4*(lane%4); the second read is 2 rows further.
 template <class S>
@@ -105,18 +112,21 @@ struct LaneOffsets {
         const int half = lane >> 5, l32 = lane & 31;
         const int krow = 32 * side + 16 * (l32 >> 4) + kperm(l32 & 15);
         k_lat = krow * S::LAT_STRIDE + 16 * half;
-        k_rope = S::ROPE_OFF + krow * S::ROPE_STRIDE + 16 * half;
+        k_rope = krow * S::ROPE_STRIDE + 16 * half;
         v = kperm(4 * half + ((lane & 15) >> 2)) * S::LAT_STRIDE + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     }
 };
 
-// Scores, softmax and P V of one LDS-resident tile for this wave.
+// Scores, softmax and P V of one LDS-resident tile for this wave: latent rows at kvl, rope
+// rows at kvr (separate LDS objects, so loads streaming into one are not taken to alias
+// reads of the other).
 //  mask(s):          applies -inf to scores of keys the row must not see (s[i] is tile
 //                    key score_key(side, half, i), for row l32);
 //  after_exchange(): runs right after the barrier that publishes the P fragments, when
 //                    every wave has finished its Q K^T reads of this tile.
 template <class S, int DL, class Mask, class Hook>
-__device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)[S::KB], f32x16 (&acc_o)[S::NB / 2],
+__device__ __forceinline__ void tile_compute(const char* kvl, const char* kvr, const bf16x8 (&qf)[S::KB],
+                                             f32x16 (&acc_o)[S::NB / 2],
                                              float& m_ref, float& l_run, float scale_log2, int wave, int side,
                                              int lane, const LaneOffsets<S>& lo, Exchange& ex, Mask&& mask,
                                              Hook&& after_exchange) {
@@ -124,8 +134,8 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
     // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
     f32x16 s = f32x16{};
     {
-        const char* kl = kvt + lo.k_lat;
-        const char* kr = kvt + lo.k_rope;
+        const char* kl = kvl + lo.k_lat;
+        const char* kr = kvr + lo.k_rope;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) {
@@ -148,7 +158,7 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
     float smax = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) smax = fmaxf(smax, s[i]);
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    smax = fmaxf(smax, half_swap(smax));
     const float mloc = smax * scale_log2;  // max over this wave's 32 keys (log2 units)
     // Fast path: P against the current reference, published with a "needs a new
     // reference" flag; the slow path (any wave flagged) agrees on the pair max first.
@@ -190,10 +200,10 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
             pk[0][j] = (__bf16)pf[j];
             pk[1][j] = (__bf16)pf[8 + j];
         }
-        __syncthreads();  // everyone has read the flags and the fast-path P
+        lds_barrier();  // everyone has read the flags and the fast-path P
         ex.Px[wave][0][lane] = __builtin_bit_cast(uint4, pk[0]);
         ex.Px[wave][1][lane] = __builtin_bit_cast(uint4, pk[1]);
-        __syncthreads();
+        lds_barrier();
     }
     float lsum = 0.0f;
 #pragma unroll
@@ -208,12 +218,12 @@ __device__ __forceinline__ void tile_compute(const char* kvt, const bf16x8 (&qf)
     // Element j of the lane's k-slice of a 16-key block is key
     // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
     __builtin_amdgcn_sched_barrier(0);
-    const char* v_own = kvt + lo.v + (32 * side) * S::LAT_STRIDE;
-    const char* v_oth = kvt + lo.v + (32 * (side ^ 1)) * S::LAT_STRIDE;
+    const char* v_own = kvl + lo.v + (32 * side) * S::LAT_STRIDE;
+    const char* v_oth = kvl + lo.v + (32 * (side ^ 1)) * S::LAT_STRIDE;
 #pragma unroll
-    for (int d = 0; d < NB0; ++d) {
+    for (int kb = 0; kb < 4; ++kb) {  // own key blocks first: the partner's P has time to arrive
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int d = 0; d < NB0; ++d) {
             const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * S::LAT_STRIDE + (side * NB0 + d) * 64;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * S::LAT_STRIDE));

@@ -193,12 +193,6 @@ __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restri
     }
 }
 
-// Value of x in lane l ^ 32: one VALU lane swap of the two half-waves, no LDS round trip.
-__device__ __forceinline__ float half_swap(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
-    return __builtin_bit_cast(float, (int)((__lane_id() < 32) ? r[1] : r[0]));
-}
-
 template <int DL, int DR>
 __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ lat, const char* __restrict__ rope,

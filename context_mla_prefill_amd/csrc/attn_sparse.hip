@@ -17,8 +17,9 @@
 // pairs as the dense kernel, running the same per-tile compute. A tile is 64 key slots:
 // first the selected-index slots in 64-wide groups (a group with no valid key is skipped),
 // then the window. Per tile:
-//   * the fp8 rows of the tile's keys are gathered HBM -> LDS staging by direct-to-LDS
-//     loads (two keys per wave-wide load) while the previous tile computes;
+//   * the fp8 rows of a tile's keys and their 64-row scales are gathered HBM -> LDS staging
+//     by direct-to-LDS loads two tiles ahead (two staging slots), so a gather has the
+//     compute of a whole tile to land;
 //   * the workgroup dequantises the staged rows once into the padded bf16 tile,
 //     bf16_rne(fp32(e4m3) * scale[row/64]);
 //   * rope rows stream straight into the tile once every wave is done with the previous
@@ -30,9 +31,20 @@ namespace {
 
 using namespace attn;
 
+constexpr int MAX_TOPK = 2048;
+constexpr int GATHER_LOADS = BN / 2 / 4 + 1;  // per wave and tile: latent loads (2 keys each) + 1 scale load
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int MAX_TOPK = 2048;
+// bf16_rne(fp32(e4m3) * sc) of the 4 E4M3FN codes of w (OCP decode on gfx950).
+__device__ __forceinline__ void dequant4(uint32_t w, float sc, __bf16* out) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    out[0] = (__bf16)(a.x * sc);
+    out[1] = (__bf16)(a.y * sc);
+    out[2] = (__bf16)(b.x * sc);
+    out[3] = (__bf16)(b.y * sc);
+}
 
 template <int DL, int DR>
 __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
@@ -42,11 +54,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
     using S = Shape<DL, DR>;
     static_assert(DL == 512, "the fp8 staging assumes 512-byte latent rows");
-    __shared__ __attribute__((aligned(1024))) char kv_tile[S::TILE_BYTES];  // dequantised bf16 tile
-    __shared__ __attribute__((aligned(1024))) uint8_t stage[BN * DL];       // fp8 rows of the next tile
-    __shared__ float stage_scale[BN];
+    __shared__ __attribute__((aligned(1024))) char kv_lat[S::ROPE_OFF];        // bf16 latent rows of the current tile
+    __shared__ __attribute__((aligned(16))) char kv_rope[BN * S::ROPE_STRIDE];  // and their rope rows
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[2][BN * DL];    // fp8 rows of the next two tiles
+    __shared__ float stage_scale[2][BN];
     __shared__ int sel[MAX_TOPK];            // this token's selected indices
-    __shared__ uint64_t tmask[2];            // valid-key bits of the current / next tile
+    __shared__ uint64_t tmask[2];            // valid-key bits per staging slot
     __shared__ Exchange ex;
 
     const int hg_count = H / BM;
@@ -70,13 +83,15 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const int p = positions[tok];
     const int head = hg * BM + pair * 32 + l32;
     const int64_t grow = (int64_t)tok * H + head;
-    // Buffer views of this request's KV rows (keys are request-relative): fp8 latent rows of
-    // DL bytes and bf16 rope rows. The caller keeps N_kv * DL below 2^32.
+    // Buffer views (keys are request-relative): fp8 latent rows of DL bytes, bf16 rope rows,
+    // and the 64-row scales of the whole cache. The caller keeps N_kv * DL below 2^32.
     const int last_key = (int)(N_kv - 1 - kv0);
     const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(lat8 + kv0 * DL), 0, (int)(uint32_t)((N_kv - kv0) * DL), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rope + kv0 * (DR * 2)), 0, (int)(uint32_t)((N_kv - kv0) * (DR * 2)), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kv_scale, 0, (int)(uint32_t)(((N_kv + 63) / 64) * 4), kBufferFlags);
 
     for (int i = tid; i < MAX_TOPK; i += NT) sel[i] = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
 
@@ -92,7 +107,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const int n_sel_tiles = (topk + BN - 1) / BN;
     const int n_tiles = n_sel_tiles + (window + BN - 1) / BN;
 
-    // Key of slot j of tile t (request-relative) and whether the slot holds a key of the set.
+    // Key of slot j of tile t (request-relative) and whether the slot holds a key of the set;
+    // tiles past the last one hold no key (their slots read key 0).
     auto slot_key = [&](int t, int j, bool& ok) -> int {
         if (t < n_sel_tiles) {
             const int e = sel[t * BN + j];
@@ -113,23 +129,29 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         }
         return t;
     };
-    // Gathers tile t: fp8 latent rows and their scales into staging, its valid-key bits.
-    auto gather_latent = [&](int t, int mslot) {
-        // wave-wide load n moves keys 2n and 2n+1 (32 lanes x 16 bytes each)
+    // Gathers tile t into staging slot b: fp8 latent rows (wave-wide load n moves keys 2n and
+    // 2n+1, 32 lanes x 16 bytes each), the 64-row scale of each key (wave w: keys 16w..16w+15)
+    // and the valid-key bits. Every wave issues exactly GATHER_LOADS loads.
+    auto gather_latent = [&](int t, int b) {
 #pragma unroll
         for (int i = 0; i < BN / 2 / 4; ++i) {
             const int n = i * 4 + wave;
-            const int j = 2 * n + half;
             bool ok;
-            const int key = min(slot_key(t, j, ok), last_key);
-            lds_dma16(lat_rsrc, (uint32_t)key * DL + l32 * 16, (char*)stage + n * 1024);
+            const int key = min(slot_key(t, 2 * n + half, ok), last_key);
+            lds_dma16(lat_rsrc, (uint32_t)key * DL + l32 * 16, (char*)stage[b] + n * 1024);
+        }
+        {
+            bool ok;
+            const int key = min(slot_key(t, 16 * wave + (lane & 15), ok), last_key);
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(scale_rsrc, (lds_void*)&stage_scale[b][16 * wave], 4,
+                                                         (uint32_t)((kv0 + key) >> 6) * 4, 0, 0, 0);
         }
         if (wave == 0) {
             bool ok;
-            const int64_t row = kv0 + min(slot_key(t, lane, ok), last_key);
-            stage_scale[lane] = kv_scale[row >> 6];
+            slot_key(t, lane, ok);
             const uint64_t bits = __ballot(ok);
-            if (lane == 0) tmask[mslot] = bits;
+            if (lane == 0) tmask[b] = bits;
         }
     };
     // Rope rows of tile t straight into the bf16 tile (7 rows of 144 bytes per load).
@@ -146,35 +168,31 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
             bool ok;
             const int key = min(slot_key(t, r < BN ? r : 0, ok), last_key);
             if (ron && r < BN)
-                lds_dma16(rope_rsrc, (uint32_t)key * (DR * 2) + rc * 16,
-                          kv_tile + S::ROPE_OFF + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
+                lds_dma16(rope_rsrc, (uint32_t)key * (DR * 2) + rc * 16, kv_rope + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
         }
     };
-    // Dequantises the staged fp8 rows into the bf16 tile: thread handles 16-byte chunks
-    // tid, tid+256, ... (consecutive lanes read consecutive LDS bytes).
-    auto dequant = [&]() {
+    // Dequantises staging slot b into the bf16 tile: thread handles 16-byte chunks tid,
+    // tid+256, ... (consecutive lanes read consecutive LDS bytes).
+    auto convert = [&](int b) {
 #pragma unroll
         for (int i = 0; i < BN * DL / 16 / NT; ++i) {
             const int k = i * NT + tid;
             const int r = k / (DL / 16);
             const int c = k - r * (DL / 16);
-            const uint4 raw = *reinterpret_cast<const uint4*>(stage + k * 16);
-            const float sc = stage_scale[r];
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+            const uint4 raw = *reinterpret_cast<const uint4*>(stage[b] + k * 16);
+            const float sc = stage_scale[b][r];
             bf16x8 o0, o1;
+            __bf16 v[16];
+            dequant4(raw.x, sc, v);
+            dequant4(raw.y, sc, v + 4);
+            dequant4(raw.z, sc, v + 8);
+            dequant4(raw.w, sc, v + 12);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[u], false);
-                const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[u], true);
-                const int e = 4 * u;
-                bf16x8& o = e < 8 ? o0 : o1;
-                const int f = e & 7;
-                o[f] = (__bf16)(a.x * sc);
-                o[f + 1] = (__bf16)(a.y * sc);
-                o[f + 2] = (__bf16)(b.x * sc);
-                o[f + 3] = (__bf16)(b.y * sc);
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = v[e];
+                o1[e] = v[8 + e];
             }
-            char* dst = kv_tile + r * S::LAT_STRIDE + c * 32;
+            char* dst = kv_lat + r * S::LAT_STRIDE + c * 32;
             *reinterpret_cast<bf16x8*>(dst) = o0;
             *reinterpret_cast<bf16x8*>(dst + 16) = o1;
         }
@@ -188,33 +206,41 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     float l_run = 0.0f;
     const LaneOffsets<S> lo(side, lane);
 
+    // Issue order keeps "all but the newest GATHER_LOADS loads" equal to "everything the
+    // current tile needs": latent(t), rope(t), latent(next).
     int t = next_live(0);
-    int ms = 0;
+    int tn = n_tiles;
+    int b = 0;
     if (t < n_tiles) {
-        gather_latent(t, ms);
+        tn = next_live(t + 1);
+        gather_latent(t, 0);
         gather_rope(t);
+        gather_latent(tn, 1);  // tn may be past the last tile: loads of key 0, never used
     }
     while (t < n_tiles) {
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gathers of tile t landed
-        __syncthreads();                     // ... and every wave's
-        dequant();
-        __syncthreads();  // bf16 tile complete; staging free
-        const uint64_t bits = tmask[ms];
-        const int tn = next_live(t + 1);
-        if (tn < n_tiles) gather_latent(tn, ms ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | GATHER_LOADS);  // vmcnt(GATHER_LOADS): tile t landed
+        __syncthreads();                                     // ... for every wave
+        convert(b);
+        const uint64_t bits = tmask[b];
+        __syncthreads();  // bf16 tile complete; staging slot b free
+        const int tnn = tn < n_tiles ? next_live(tn + 1) : n_tiles;
         auto keymask = [&](f32x16& s) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = (bits >> score_key(side, half, i)) & 1 ? s[i] : -INFINITY;
         };
-        auto rope_next = [&] {
+        auto prefetch = [&] {  // after every wave's Q K^T reads of tile t
             if (tn < n_tiles) gather_rope(tn);
+            gather_latent(tnn, b);
         };
-        tile_compute<S, DL>(kv_tile, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex, keymask, rope_next);
+        tile_compute<S, DL>(kv_lat, kv_rope, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex, keymask,
+                            prefetch);
         t = tn;
-        ms ^= 1;
+        tn = tnn;
+        b ^= 1;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the unused last gather landed before LDS is released
     write_rows<S, DL>(acc_o, m_ref, l_run, true, grow, wave, side, lane, ex, o_out, lse_out);
 }
 

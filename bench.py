@@ -250,6 +250,13 @@ def main():
                   "traffic": merge_traffic},
         "setup_s": round(setup_s, 1),
     }
+    if sparse:
+        # algorithmic gather: every key of a query's set once per 64-head workgroup, fp8
+        # latent row + bf16 rope row + its fp32 scale
+        gbytes_r = [float(n_keys[g].sum()) * (w.H // 64) * (w.Dl + 2 * w.Dr + 4) for g in gidx_r]
+        gbs = float(np.mean([b / (t * 1e-3) / 1e9 for b, t in zip(gbytes_r, t_rank)]))
+        out["gather"] = {"bytes_per_rank": [round(b) for b in gbytes_r], "GB/s": round(gbs, 1),
+                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
     if args.calib_copy:
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)

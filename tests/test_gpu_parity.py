@@ -374,6 +374,35 @@ def test_sparse_small_all_rows(gpu_lib):
     run.check_values(np.arange(w.T_glob))
 
 
+SPARSE_EDGE = {
+    # seed: (q_lens, kv_lens, P, H, topk, window, shuffle the selected indices)
+    211: ([900, 1, 300], [900, 700, 300], 2, 128, 128, 32, False),  # 2 head groups, a decode row
+    212: ([1000], [1000], 2, 64, 192, 0, True),                      # top-k only, unsorted rows
+    213: ([640, 5], [640, 5], 3, 64, 1, 96, False),                  # window only (one pad column), short prefill
+    214: ([777], [1200], 2, 64, 64, 200, True),                      # continuation, wide window overlapping top-k
+}
+
+
+@pytest.mark.parametrize("seed", sorted(SPARSE_EDGE))
+def test_sparse_edge_cases(gpu_lib, seed):
+    """Sparse shapes beyond the two workloads: several head groups, decode and short-prefill
+    rows, top-k only, window only, unsorted selected indices (the kernel may not depend on
+    their order), kv_len > q_len; every row of every rank and the merge."""
+    q, kv, P, H, topk, window, shuffle = SPARSE_EDGE[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64, topk=topk, window=window, kv_dtype="fp8",
+                     latent_std=1.0)
+    rows = synth.topk_rows(w)
+    if topk == 1:
+        rows[:] = -1  # window only
+    if shuffle:
+        rng = np.random.default_rng(seed)
+        rows = np.stack([rng.permutation(r) for r in rows]).astype(np.int32)
+    run = SparseRun(w, topk_rows=rows)
+    check_plan(run.pl, run.plan)
+    run.check_insert()
+    run.check_values(np.arange(w.T_glob))
+
+
 def test_sparse128k_p2_sampled(gpu_lib):
     """128K tokens, P=2, 64 heads, top-2048 + window 128, fp8 KV: plan and insert in full,
     values on the ends of every chunk plus random tokens, all rows finite."""

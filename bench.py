@@ -52,10 +52,10 @@ def sparse_set_sizes(topk_rows: np.ndarray, w) -> np.ndarray:
     return out
 
 
-def merge_bytes(merge_src: np.ndarray, H: int, Dv: int) -> float:
-    """Bytes the merge must move: each contributor row (O bf16 + LSE fp32) read, each
-    output row written, plus the map."""
-    n_contrib = int((merge_src >= 0).sum())
+def merge_bytes(merge_src: np.ndarray, H: int, Dv: int, kv_splits: int = 1) -> float:
+    """Bytes the merge must move: each contributor row (O bf16 + LSE fp32; one per rank row
+    and key split) read, each output row written, plus the map."""
+    n_contrib = int((merge_src >= 0).sum()) * kv_splits
     T, P = merge_src.shape
     return float(n_contrib * H * (2 * Dv + 4) + T * H * (2 * Dv + 4) + T * P * 4)
 
@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-splits", type=int, default=1,
+                    help="cut every row's keys into this many ranges (split-KV partials, merged with the ranks)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
                          "(a kernel of known byte count for scaling HBM traffic counters)")
@@ -173,10 +175,11 @@ def main():
     del q
     kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
     kv_rope = rope_full.clone()
-    bufs = pp.alloc_step(pl, w.H, w.Dl)
+    S = args.kv_splits
+    bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=S)
     kv_dtype = _lib.MLA_KV_FP8_E4M3 if sparse else _lib.MLA_KV_BF16
     args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, kv_dtype=kv_dtype,
-                              kv_scale=kv_scale, topk=w.topk, window=w.window) for r in range(w.P)]
+                              kv_scale=kv_scale, topk=w.topk, window=w.window, kv_splits=S) for r in range(w.P)]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -198,7 +201,7 @@ def main():
                 ev[r][1].record(stream)
         if ev:
             ev[w.P][0].record(stream)
-        pp.run_merge(pl, bufs, sink, w.H, w.Dl)
+        pp.run_merge(pl, bufs, sink, w.H, w.Dl, kv_splits=S)
         if ev:
             ev[w.P][1].record(stream)
 
@@ -226,7 +229,7 @@ def main():
     t_merge = float(np.mean([events[k][w.P][0].elapsed_time(events[k][w.P][1]) for k in range(args.steps)]))
     avg_launch_ms = float(np.mean(t_rank))
     achieved = (flops_step / w.P) / (avg_launch_ms * 1e-3) / 1e12
-    mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl)
+    mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl, S)
     att_traffic, merge_traffic = measured_traffic(args.workload)
 
     out = {
@@ -238,7 +241,8 @@ def main():
         "dtype": "fp8-e4m3 KV dequantised to bf16, bf16 MFMA" if sparse else "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 bf16 q/latent/rope, N(0,1) sink)",
         "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
-                   "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU"},
+                   "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU",
+                   **({"kv_splits": S} if S > 1 else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": att_traffic},
         "attention": {"rank_ms": [round(x, 3) for x in t_rank],

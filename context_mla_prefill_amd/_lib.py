@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmla_pcp.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ("mla_pcp_abi_version", "mla_pcp_last_error", "pcp_plan_sizes", "pcp_partition",
             "pcp_kv_insert", "mla_prefill_partial", "pcp_lse_merge")
@@ -45,6 +45,7 @@ class mla_partial_args(ctypes.Structure):
         ("topk", _i32), ("window", _i32), ("n_vrows", _i32), ("T_loc", _i32), ("H", _i32),
         ("D_latent", _i32), ("D_rope", _i32), ("kv_dtype", _i32), ("N_kv", _i64),
         ("scale", ctypes.c_float), ("o_partial", _p), ("lse", _p),
+        ("kv_splits", _i32), ("split_stride", _i64), ("vrow_kv_len", _p),
     ]
 
 
@@ -71,7 +72,7 @@ def load():
     lib.mla_prefill_partial.restype = ctypes.c_int
     lib.mla_prefill_partial.argtypes = [ctypes.POINTER(mla_partial_args), _p]
     lib.pcp_lse_merge.restype = ctypes.c_int
-    lib.pcp_lse_merge.argtypes = [_p, _p, _p, _i32, _i64, _i32, _i32, _i64, _p, _p, _p, _p]
+    lib.pcp_lse_merge.argtypes = [_p, _p, _p, _i32, _i64, _i32, _i32, _i64, _i32, _i64, _p, _p, _p, _p]
     if lib.mla_pcp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"ABI mismatch: library {lib.mla_pcp_abi_version()} binding {ABI_VERSION}")
     _lib = lib
@@ -140,13 +141,15 @@ def pcp_kv_insert(local_latent, local_rope, slot, T_loc, D_latent, D_rope, kv_dt
 
 def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positions, n_vrows, T_loc, H,
                       D_latent, D_rope, scale, o_partial, lse, N_kv, kv_dtype=MLA_KV_BF16, kv_scale=None,
-                      topk_idx=None, topk=0, window=0) -> mla_partial_args:
+                      topk_idx=None, topk=0, window=0, kv_splits=1, split_stride=0,
+                      vrow_kv_len=None) -> mla_partial_args:
     return mla_partial_args(
         q=_ptr(q), latent_kv=_ptr(latent_kv), kv_scale=_ptr(kv_scale), rope_k=_ptr(rope_k),
         cu_seqlens_q=_ptr(cu_seqlens_q), vrow_kv_start=_ptr(vrow_kv_start), positions=_ptr(positions),
         topk_idx=_ptr(topk_idx), topk=topk, window=window, n_vrows=n_vrows, T_loc=T_loc, H=H,
         D_latent=D_latent, D_rope=D_rope, kv_dtype=kv_dtype, N_kv=N_kv, scale=float(scale),
-        o_partial=_ptr(o_partial), lse=_ptr(lse))
+        o_partial=_ptr(o_partial), lse=_ptr(lse), kv_splits=kv_splits, split_stride=split_stride,
+        vrow_kv_len=_ptr(vrow_kv_len))
 
 
 def mla_prefill_partial(args: mla_partial_args, stream=None):
@@ -155,7 +158,7 @@ def mla_prefill_partial(args: mla_partial_args, stream=None):
 
 
 def pcp_lse_merge(o_cat, lse_cat, merge_src, P, T_glob, H, D_v, R_total, sink, o_out, lse_out,
-                  stream=None):
+                  stream=None, kv_splits=1, split_stride=0):
     st = load().pcp_lse_merge(_ptr(o_cat), _ptr(lse_cat), _ptr(merge_src), P, T_glob, H, D_v, R_total,
-                              _ptr(sink), _ptr(o_out), _ptr(lse_out), _stream(stream))
+                              kv_splits, split_stride, _ptr(sink), _ptr(o_out), _ptr(lse_out), _stream(stream))
     _check(st, "pcp_lse_merge")

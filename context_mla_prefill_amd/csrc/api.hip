@@ -155,6 +155,14 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
     } else if (a->kv_dtype != MLA_KV_BF16) {
         return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: dense path takes bf16 KV");
     }
+    if (a->kv_splits < 1 || a->kv_splits > 64)
+        return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: kv_splits=%d outside 1..64", a->kv_splits);
+    if (a->kv_splits > 1 && (a->split_stride < a->T_loc || !a->vrow_kv_len ||
+                             a->split_stride * (a->kv_splits - 1) + a->T_loc > INT32_MAX / a->H))
+        return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: split KV needs split_stride >= T_loc, "
+                                         "vrow_kv_len and outputs within int32 rows*H");
+    if ((((int64_t)a->T_loc * a->H + 63) / 64 + a->n_vrows) * a->kv_splits > INT32_MAX)
+        return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: too many workgroups");
     if (a->T_loc == 0) return MLA_OK;
     if (!a->q || !a->latent_kv || !a->rope_k || !a->cu_seqlens_q || !a->vrow_kv_start ||
         !a->positions || !a->o_partial || !a->lse)
@@ -172,10 +180,14 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
 
 mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
                          int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
-                         const float* sink, void* o_out, float* lse_out, void* stream) {
+                         int32_t kv_splits, int64_t split_stride, const float* sink, void* o_out,
+                         float* lse_out, void* stream) {
     if (P < 1 || P > 64 || T_glob < 0 || H < 1 || R_total < 0 || T_glob * (int64_t)H > INT32_MAX ||
         R_total * (int64_t)H > INT32_MAX)
         return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: sizes out of range (P=%d H=%d)", P, H);
+    if (kv_splits < 1 || P * kv_splits > 64 || split_stride < 0)
+        return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: kv_splits=%d with P=%d (P*kv_splits <= 64)",
+                    kv_splits, P);
     if (D_v < 8 || D_v > 1024 || D_v % 8 != 0)
         return fail(MLA_ERR_UNSUPPORTED, "pcp_lse_merge: D_v=%d must be a multiple of 8 in 8..1024", D_v);
     if (H > 128) return fail(MLA_ERR_UNSUPPORTED, "pcp_lse_merge: H=%d above 128", H);
@@ -184,8 +196,8 @@ mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t*
         return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: null pointer");
     if ((o_cat && !aligned16(o_cat)) || !aligned16(o_out))
         return fail(MLA_ERR_INVALID_ARG, "pcp_lse_merge: O buffers must be 16-byte aligned");
-    hipError_t e = launch_merge(o_cat, lse_cat, merge_src, P, T_glob, H, D_v, R_total, sink, o_out,
-                                lse_out, (hipStream_t)stream);
+    hipError_t e = launch_merge(o_cat, lse_cat, merge_src, P, T_glob, H, D_v, R_total, kv_splits, split_stride,
+                                sink, o_out, lse_out, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "pcp_lse_merge: %s", hipGetErrorString(e));
     return MLA_OK;
 }

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ lat, const char* __restrict__ rope,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, int n_vrows, int H, int64_t N_kv, float scale_log2,
-    __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
+    __bf16* __restrict__ o_out, float* __restrict__ lse_out, int kv_splits, int64_t split_stride,
+    const int32_t* __restrict__ vrow_kv_len) {
     using T = DenseTile<DL, DR>;
     __shared__ __attribute__((aligned(1024))) char kv_lds0[T::TILE_BYTES];  // KV tile double buffer:
     __shared__ __attribute__((aligned(1024))) char kv_lds1[T::TILE_BYTES];  // two separate objects
@@ -208,8 +209,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     __shared__ int s_maxpos[NT / 64];
     int* sh = reinterpret_cast<int*>(&Px[0][0][0]);  // scan scratch, used before the KV loop only
 
+    // workgroup = (row tile, key split); splits of one tile are adjacent in launch order
+    const int ridx = (int)blockIdx.x / kv_splits;
+    const int split = (int)blockIdx.x - ridx * kv_splits;
     int v, tile;
-    find_tile((int)blockIdx.x, cu, n_vrows, H, sh, v, tile);
+    find_tile(ridx, cu, n_vrows, H, sh, v, tile);
     v = __builtin_amdgcn_readfirstlane(v);  // workgroup-uniform: keep it in SGPRs
     tile = __builtin_amdgcn_readfirstlane(tile);
     if (v < 0) return;
@@ -248,7 +252,18 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     int kv_hi = s_maxpos[0];
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) kv_hi = max(kv_hi, s_maxpos[w]);
-    kv_hi = __builtin_amdgcn_readfirstlane(kv_hi + 1);
+    kv_hi = kv_hi + 1;
+    // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
+    int key_lo = 0;
+    if (kv_splits > 1) {
+        const int n = (vrow_kv_len[v] + BN - 1) / BN;
+        key_lo = BN * (int)(((int64_t)split * n) / kv_splits);
+        kv_hi = min(kv_hi, BN * (int)(((int64_t)(split + 1) * n) / kv_splits));
+        o_out += split * split_stride * H * DL;
+        lse_out += split * split_stride * H;
+    }
+    kv_hi = __builtin_amdgcn_readfirstlane(kv_hi);
+    const int kt0 = __builtin_amdgcn_readfirstlane(key_lo / BN);
     // smallest position among this wave's rows: key blocks at or below it need no mask
     int pmin = valid ? pos : INT32_MAX;
 #pragma unroll
@@ -425,19 +440,21 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         }
     };
 
-    if constexpr (T::WIDE) {
-        const WideTile<T, DL, DR> src(lat, rope, kv0, 0, last);
+    if (kt0 < n_tiles) {  // workgroup-uniform; an empty key range leaves O = 0, LSE = -inf
+        if constexpr (T::WIDE) {
+            const WideTile<T, DL, DR> src(lat, rope, kv0, kt0, last);
 #pragma unroll
-        for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(kv_lds0, wave, lane, i);
+            for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(kv_lds0, wave, lane, i);
 #pragma unroll
-        for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(kv_lds0, wave, lane, u);
-    } else {
-        narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, kv0, 0, last, wave, lane);
-    }
-    for (int kt = 0; kt < n_tiles; kt += 2) {
-        tile_step(kv_lds0, kv_lds1, kt);
-        if (kt + 1 >= n_tiles) break;
-        tile_step(kv_lds1, kv_lds0, kt + 1);
+            for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(kv_lds0, wave, lane, u);
+        } else {
+            narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, kv0, kt0, last, wave, lane);
+        }
+        for (int kt = kt0; kt < n_tiles; kt += 2) {
+            tile_step(kv_lds0, kv_lds1, kt);
+            if (kt + 1 >= n_tiles) break;
+            tile_step(kv_lds1, kv_lds0, kt + 1);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // loads issued after the last tile landed before LDS is released
 
@@ -467,11 +484,11 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 
 template <int DL, int DR>
 hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
-    const int64_t grid = ((int64_t)a.T_loc * a.H + BM - 1) / BM + a.n_vrows;
+    const int64_t grid = (((int64_t)a.T_loc * a.H + BM - 1) / BM + a.n_vrows) * a.kv_splits;
     hipLaunchKernelGGL((dense_partial_kernel<DL, DR>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.n_vrows, a.H, a.N_kv, a.scale * kLog2e,
-                       (__bf16*)a.o_partial, a.lse);
+                       (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len);
     return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ lat8, const float* __restrict__ kv_scale,
     const char* __restrict__ rope, const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, const int32_t* __restrict__ topk_idx, int topk, int window,
-    int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out) {
+    int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out,
+    int kv_splits, int64_t split_stride, const int32_t* __restrict__ vrow_kv_len) {
     using S = Shape<DL, DR>;
     static_assert(DL == 512, "the fp8 staging assumes 512-byte latent rows");
     __shared__ __attribute__((aligned(1024))) char kv_lat[S::ROPE_OFF];        // bf16 latent rows of the current tile
@@ -62,9 +63,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     __shared__ uint64_t tmask[2];            // valid-key bits per staging slot
     __shared__ Exchange ex;
 
+    // workgroup = (token, 64-head group, key split); splits of one row are adjacent
     const int hg_count = H / BM;
-    const int tok = blockIdx.x / hg_count;
-    const int hg = blockIdx.x - tok * hg_count;
+    const int ridx = (int)blockIdx.x / kv_splits;
+    const int split = (int)blockIdx.x - ridx * kv_splits;
+    const int tok = ridx / hg_count;
+    const int hg = ridx - tok * hg_count;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int pair = wave >> 1;
@@ -81,6 +85,15 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     }
     const int64_t kv0 = vrow_kv_start[lo_v];
     const int p = positions[tok];
+    // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
+    int key_lo = 0, key_hi = INT32_MAX;
+    if (kv_splits > 1) {
+        const int n = (vrow_kv_len[lo_v] + BN - 1) / BN;
+        key_lo = BN * (int)(((int64_t)split * n) / kv_splits);
+        key_hi = BN * (int)(((int64_t)(split + 1) * n) / kv_splits);
+        o_out += split * split_stride * H * DL;
+        lse_out += split * split_stride * H;
+    }
     const int head = hg * BM + pair * 32 + l32;
     const int64_t grow = (int64_t)tok * H + head;
     // Buffer views (keys are request-relative): fp8 latent rows of DL bytes, bf16 rope rows,
@@ -112,12 +125,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     auto slot_key = [&](int t, int j, bool& ok) -> int {
         if (t < n_sel_tiles) {
             const int e = sel[t * BN + j];
-            ok = e >= 0 && e <= p && (window == 0 || e < win_lo);
+            ok = e >= key_lo && e < key_hi && e <= p && (window == 0 || e < win_lo);
             return ok ? e : 0;
         }
         const int w = (t - n_sel_tiles) * BN + j;
         const int k = win_lo + w;
-        ok = window > 0 && w < window && k <= p;
+        ok = window > 0 && w < window && k <= p && k >= key_lo && k < key_hi;
         return ok ? k : 0;
     };
     // Next tile index >= t that holds at least one key (n_tiles if none); workgroup-uniform.
@@ -247,11 +260,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
 }  // namespace
 
 hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream) {
-    const int64_t grid = (int64_t)a.T_loc * (a.H / BM);
+    const int64_t grid = (int64_t)a.T_loc * (a.H / BM) * a.kv_splits;
     hipLaunchKernelGGL((sparse_partial_kernel<512, 64>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const uint8_t*)a.latent_kv, a.kv_scale, (const char*)a.rope_k,
                        a.cu_seqlens_q, a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H,
-                       a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse);
+                       a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride,
+                       a.vrow_kv_len);
     return hipGetLastError();
 }
 

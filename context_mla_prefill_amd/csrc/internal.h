@@ -27,7 +27,8 @@ hipError_t launch_kv_insert(const void* local_latent, const void* local_rope, co
 
 hipError_t launch_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
                         int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
-                        const float* sink, void* o_out, float* lse_out, hipStream_t stream);
+                        int32_t kv_splits, int64_t split_stride, const float* sink, void* o_out,
+                        float* lse_out, hipStream_t stream);
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream);

@@ -32,18 +32,22 @@ constexpr int UNROLL = 4;  // vectors per thread in flight
 
 __global__ __launch_bounds__(NT) void merge_kernel(
     const u32x4* __restrict__ o_cat, const float* __restrict__ lse_cat,
-    const int32_t* __restrict__ merge_src, int P, int H, int G, int64_t R_total,
+    const int32_t* __restrict__ merge_src, int P, int S, int64_t split_stride, int H, int G, int64_t R_total,
     const float* __restrict__ sink, u32x4* __restrict__ o_out, float* __restrict__ lse_out) {
     __shared__ int rows[MAXP];
     __shared__ int n_rows;
     __shared__ float wts[MAXP][MAXH];  // exp(L_k - M) / D per contributor and head
     const int64_t t = blockIdx.x;
     const int tid = threadIdx.x;
-    if (tid == 0) {
+    if (tid == 0) {  // contributors: every rank's row, in each of its S split slices
         int n = 0;
         for (int k = 0; k < P; ++k) {
-            const int64_t r = merge_src[t * P + k];
-            if (r >= 0 && r < R_total) rows[n++] = (int)r;
+            const int64_t r0 = merge_src[t * P + k];
+            if (r0 < 0) continue;
+            for (int s = 0; s < S; ++s) {
+                const int64_t r = r0 + s * split_stride;
+                if (r < R_total) rows[n++] = (int)r;
+            }
         }
         n_rows = n;
     }
@@ -111,10 +115,11 @@ __global__ __launch_bounds__(NT) void merge_kernel(
 
 hipError_t launch_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
                         int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
-                        const float* sink, void* o_out, float* lse_out, hipStream_t stream) {
+                        int32_t kv_splits, int64_t split_stride, const float* sink, void* o_out,
+                        float* lse_out, hipStream_t stream) {
     const int G = D_v / 8;
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)T_glob), dim3(NT), 0, stream, (const u32x4*)o_cat, lse_cat,
-                       merge_src, P, H, G, R_total, sink, (u32x4*)o_out, lse_out);
+                       merge_src, P, kv_splits, split_stride, H, G, R_total, sink, (u32x4*)o_out, lse_out);
     return hipGetLastError();
 }
 

@@ -98,23 +98,26 @@ class StepBuffers:
     lse: torch.Tensor  # [T_glob, H] fp32
 
 
-def alloc_step(pl: DevicePlan, H: int, Dl: int, device="cuda") -> StepBuffers:
-    return StepBuffers(o_cat=torch.empty(pl.T_total, H, Dl, dtype=BF16, device=device),
-                       lse_cat=torch.empty(pl.T_total, H, dtype=torch.float32, device=device),
+def alloc_step(pl: DevicePlan, H: int, Dl: int, device="cuda", kv_splits: int = 1) -> StepBuffers:
+    """Partial outputs of every rank (kv_splits slices of T_total rows each) and the merged output."""
+    return StepBuffers(o_cat=torch.empty(kv_splits * pl.T_total, H, Dl, dtype=BF16, device=device),
+                       lse_cat=torch.empty(kv_splits * pl.T_total, H, dtype=torch.float32, device=device),
                        o=torch.empty(pl.T_glob, H, Dl, dtype=BF16, device=device),
                        lse=torch.empty(pl.T_glob, H, dtype=torch.float32, device=device))
 
 
 def partial_args(pl: DevicePlan, r: int, ri: RankInputs, kv_latent, kv_rope, bufs: StepBuffers, H, Dl, Dr,
-                 scale, kv_dtype=_lib.MLA_KV_BF16, kv_scale=None, topk=0, window=0):
+                 scale, kv_dtype=_lib.MLA_KV_BF16, kv_scale=None, topk=0, window=0, kv_splits=1):
     rows = pl.rank_rows(r)
     return _lib.make_partial_args(
         q=ri.q, latent_kv=kv_latent, rope_k=kv_rope, cu_seqlens_q=pl.cu_q[r], vrow_kv_start=pl.vrow_kv_start[r],
         positions=pl.positions[rows], n_vrows=pl.n_vrows, T_loc=pl.T_loc[r], H=H, D_latent=Dl, D_rope=Dr,
         scale=scale, o_partial=bufs.o_cat[rows], lse=bufs.lse_cat[rows], N_kv=int(kv_latent.shape[0]),
-        kv_dtype=kv_dtype, kv_scale=kv_scale, topk_idx=ri.topk, topk=topk, window=window)
+        kv_dtype=kv_dtype, kv_scale=kv_scale, topk_idx=ri.topk, topk=topk, window=window,
+        kv_splits=kv_splits, split_stride=pl.T_total if kv_splits > 1 else 0,
+        vrow_kv_len=pl.vrow_kv_len[r] if kv_splits > 1 else None)
 
 
-def run_merge(pl: DevicePlan, bufs: StepBuffers, sink, H: int, Dl: int, stream=None):
-    _lib.pcp_lse_merge(bufs.o_cat, bufs.lse_cat, pl.merge_src, pl.P, pl.T_glob, H, Dl, pl.T_total, sink,
-                       bufs.o, bufs.lse, stream)
+def run_merge(pl: DevicePlan, bufs: StepBuffers, sink, H: int, Dl: int, stream=None, kv_splits: int = 1):
+    _lib.pcp_lse_merge(bufs.o_cat, bufs.lse_cat, pl.merge_src, pl.P, pl.T_glob, H, Dl, kv_splits * pl.T_total, sink,
+                       bufs.o, bufs.lse, stream, kv_splits=kv_splits, split_stride=pl.T_total)

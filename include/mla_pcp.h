@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define MLA_PCP_ABI_VERSION 1
+#define MLA_PCP_ABI_VERSION 2
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -140,6 +140,15 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
  *   S_j = scale * <q[i][h], key_j>; O = softmax(S) @ latent (bf16, round to nearest
  *   even); LSE = log(sum_j exp(S_j)) (fp32, natural log). No sink.
  * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]).
+ * Split KV (kv_splits = S > 1): the key set of a row is cut by key position into S
+ *   ranges and each range gives its own partial (O, LSE), written at split slice s of
+ *   the outputs; merging the S partials (pcp_lse_merge with the same S) gives the
+ *   unsplit result. With L = vrow_kv_len[v] and n = ceil(L / 64) tiles, range s holds
+ *   request-relative keys [64 * floor(s * n / S), 64 * floor((s + 1) * n / S)), the
+ *   last one ending at L. A range with no key of the row gives O = 0, LSE = -inf. The
+ *   per-rank partial of the "local partial, global LSE merge" reading ("[DeepSeekV4][PCP]
+ *   Enable context-parallel prefill for hybrid KV and MegaMoE", "Purpose") applied to
+ *   key ranges instead of ranks: long rows are spread over more workgroups.
  */
 typedef struct mla_partial_args {
     const void* q;               /* device bf16 [T_loc][H][D_latent + D_rope]            */
@@ -161,11 +170,17 @@ typedef struct mla_partial_args {
     int32_t kv_dtype;            /* MLA_KV_BF16 or MLA_KV_FP8_E4M3                         */
     int64_t N_kv;                /* rows of latent_kv / rope_k                             */
     float scale;                 /* softmax scale                                          */
-    void* o_partial;             /* device bf16 out [T_loc][H][D_latent]                   */
-    float* lse;                  /* device fp32 out [T_loc][H]                             */
+    void* o_partial;             /* device bf16 out [T_loc][H][D_latent] (split slice 0)  */
+    float* lse;                  /* device fp32 out [T_loc][H] (split slice 0)             */
+    int32_t kv_splits;           /* key ranges per row, 1..64 (1 = no split)               */
+    int64_t split_stride;        /* rows from one split slice of o_partial / lse to the
+                                    next (>= T_loc when kv_splits > 1)                    */
+    const int32_t* vrow_kv_len;  /* device [n_vrows] last position of the virtual row + 1,
+                                    as pcp_partition writes it (needed when kv_splits > 1) */
 } mla_partial_args;
 
-/* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales);
+/* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales,
+ * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1);
  * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
  * bf16 KV, with H not a multiple of 64 or with N_kv >= 2^23 rows, dense with fp8 KV,
  * dtype); HIP.
@@ -179,7 +194,8 @@ mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
  * MegaMoE", "Purpose" and "Main challenges" (merge LSE/output globally, apply attn_sink
  * only once, never per rank); order restore from "[Core] Add MRV2 virtual-batch PCP for
  * MLA", "DualChunkSwap partitioning".
- * For token t, head h, contributors k (rows merge_src[t][k] >= 0) and sink s_h:
+ * For token t, head h, contributors k (rows merge_src[t][k] >= 0, each with kv_splits
+ * split slices: rows merge_src[t][k] + s * split_stride, s < kv_splits) and sink s_h:
  *   M = max(s_h, max_k L_k); D = exp(s_h - M) + sum_k exp(L_k - M);
  *   O = sum_k exp(L_k - M) O_k / D (bf16 RNE); LSE = M + log D (fp32).
  *
@@ -190,12 +206,14 @@ mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
  *  sink      device fp32 [H] or NULL (no sink).
  *  o_out     device bf16 out [T_glob][H][D_v]; lse_out device fp32 [T_glob][H] or NULL.
  * A row with no contributor gets O = 0 and LSE = s_h (-inf without a sink).
- * Errors: INVALID_ARG (null, sizes, P out of 1..64, misalignment); UNSUPPORTED (D_v not
- * a multiple of 8 in 8..1024, H above 128); HIP.
+ * Errors: INVALID_ARG (null, sizes, P out of 1..64, kv_splits < 1, P * kv_splits above
+ * 64, split_stride < 0, misalignment); UNSUPPORTED (D_v not a multiple of 8 in 8..1024,
+ * H above 128); HIP.
  */
 mla_status pcp_lse_merge(const void* o_cat, const float* lse_cat, const int32_t* merge_src,
                          int32_t P, int64_t T_glob, int32_t H, int32_t D_v, int64_t R_total,
-                         const float* sink, void* o_out, float* lse_out, void* stream);
+                         int32_t kv_splits, int64_t split_stride, const float* sink, void* o_out,
+                         float* lse_out, void* stream);
 
 #ifdef __cplusplus
 }

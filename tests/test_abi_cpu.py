@@ -108,6 +108,10 @@ def test_partial_validation_errors():
         _lib.MLA_ERR_UNSUPPORTED
     assert call(_args(**ok, topk_idx=f, topk=64, window=128, kv_dtype=1, kv_scale=f, H=64, N_kv=1 << 23))[0] == \
         _lib.MLA_ERR_UNSUPPORTED  # sparse KV rows addressed by 32-bit byte offsets
+    assert call(_args(**ok, kv_splits=0))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, kv_splits=65))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert call(_args(**ok, kv_splits=2, split_stride=4))[0] == _lib.MLA_ERR_INVALID_ARG  # no vrow_kv_len
+    assert call(_args(**ok, kv_splits=2, split_stride=3, vrow_kv_len=f))[0] == _lib.MLA_ERR_INVALID_ARG  # < T_loc
     st, msg = call(_args(**ok, D_rope=32))
     assert st == _lib.MLA_ERR_UNSUPPORTED and "dims" in msg
     # empty shard: nothing to do, OK without touching any pointer
@@ -124,6 +128,9 @@ def test_merge_and_insert_validation_errors():
     assert m(merge_src=None)[0] == _lib.MLA_ERR_INVALID_ARG
     assert m(o_out=_P(FAKE + 4))[0] == _lib.MLA_ERR_INVALID_ARG
     assert m(T_glob=0)[0] == 0
+    assert m(kv_splits=0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert m(P=8, kv_splits=9)[0] == _lib.MLA_ERR_INVALID_ARG  # 72 contributors per token
+    assert m(kv_splits=2, split_stride=-1)[0] == _lib.MLA_ERR_INVALID_ARG
     ins = lambda **kw: _status(lambda: _lib.pcp_kv_insert(**{**dict(
         local_latent=f, local_rope=f, slot=f, T_loc=4, D_latent=512, D_rope=64, kv_dtype=0, N_kv=8,
         kv_latent=f, kv_rope=f, stream=0), **kw}))

@@ -50,10 +50,11 @@ def check_plan(pl, plan):
 class DenseRun:
     """Runs partition -> insert -> P partials -> merge for a bf16 dense workload."""
 
-    def __init__(self, w):
+    def __init__(self, w, kv_splits=1):
         self.w = w
+        self.kv_splits = kv_splits
         self.plan = hp.oracle_plan(w)
-        print(f"[run] workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
+        print(f"[run] workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv} kv_splits={kv_splits}", flush=True)
         self.q_bits = synth.q_rows(w)
         self.lat_bits = synth.latent_rows(w)
         self.rope_bits = synth.rope_rows(w)
@@ -67,7 +68,7 @@ class DenseRun:
         new_rows = torch.unique(pl.slot.long())
         self.kv_lat.view(torch.int16)[new_rows] = 0x7FC0
         self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
-        self.bufs = pp.alloc_step(pl, w.H, w.Dl)
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
         self.sink_d = torch.from_numpy(self.sink).cuda()
         ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full) for r in range(w.P)]
         # every rank's rows reach the full KV (the all-gather) before any rank attends
@@ -75,9 +76,10 @@ class DenseRun:
             _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
                                _lib.MLA_KV_BF16, w.N_kv, self.kv_lat, self.kv_rope)
         for r, ri in enumerate(ranks):
-            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale)
+            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                   kv_splits=kv_splits)
             _lib.mla_prefill_partial(args)
-        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
         self.lat_full, self.rope_full = lat_full, rope_full
 
@@ -285,8 +287,9 @@ SPARSE_O_TOL = 3e-2
 class SparseRun:
     """partition -> fp8 insert -> P sparse partials -> merge for an fp8 top-k workload."""
 
-    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None):
+    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None, kv_splits=1):
         self.w = w
+        self.kv_splits = kv_splits
         self.plan = hp.oracle_plan(w)
         print(f"[run] sparse workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
         self.q_bits = synth.q_rows(w)
@@ -307,7 +310,7 @@ class SparseRun:
         new_rows = torch.unique(pl.slot.long())
         self.kv_lat[new_rows] = 0x7F
         self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
-        self.bufs = pp.alloc_step(pl, w.H, w.Dl)
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
         self.sink_d = torch.from_numpy(self.sink).cuda()
         ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk_d) for r in range(w.P)]
         for r, ri in enumerate(ranks):
@@ -315,9 +318,10 @@ class SparseRun:
                                _lib.MLA_KV_FP8_E4M3, w.N_kv, self.kv_lat, self.kv_rope)
         for r, ri in enumerate(ranks):
             args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk, window=w.window)
+                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk, window=w.window,
+                                   kv_splits=kv_splits)
             _lib.mla_prefill_partial(args)
-        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
         self.lat_full, self.rope_full = lat_full, rope_full
 
@@ -401,6 +405,96 @@ def test_sparse_edge_cases(gpu_lib, seed):
     check_plan(run.pl, run.plan)
     run.check_insert()
     run.check_values(np.arange(w.T_glob))
+
+
+def split_ranges(L, S):
+    """Key ranges of the split-KV call for a virtual row whose last position is L-1:
+    n = ceil(L/64) tiles, range s = request-relative keys [64*floor(s*n/S), 64*floor((s+1)*n/S))."""
+    n = -(-L // 64)
+    return [(64 * (s * n // S), 64 * ((s + 1) * n // S)) for s in range(S)]
+
+
+def check_split_partials(run, tokens, key_rows, o_tol):
+    """Every split slice of every rank's partial rows of the given tokens against the oracle
+    restricted to that split's keys (no sink); a split with no key of the row must give
+    O = 0 and LSE = -inf. key_rows(t) -> (request-relative keys, latent fp64, rope fp64)."""
+    w, plan, S = run.w, run.plan, run.kv_splits
+    o_cat = on.bf16_to_f64(host_bits(run.bufs.o_cat))
+    lse_cat = run.bufs.lse_cat.cpu().numpy()
+    q = on.bf16_to_f64(run.q_bits)
+    tokset = set(int(t) for t in tokens)
+    for r, rp in enumerate(plan.ranks):
+        vrow = np.searchsorted(rp.cu_seqlens_q, np.arange(rp.T_loc), side="right") - 1
+        for i, g in enumerate(rp.local_gidx):
+            g = int(g)
+            if g not in tokset:
+                continue
+            keys, lat, rope = key_rows(g)
+            for s, (lo, hi) in enumerate(split_ranges(int(rp.vrow_kv_len[vrow[i]]), S)):
+                row = s * run.pl.T_total + plan.row_off[r] + i
+                sel = (keys >= lo) & (keys < hi)
+                if not sel.any():
+                    assert np.all(o_cat[row] == 0) and np.all(np.isneginf(lse_cat[row])), (g, s)
+                    continue
+                o0, lse0, _, _ = oa.attend_keyset(q[g], lat[sel], rope[sel], float(w.scale))
+                hp.compare(f"token {g} rank {r} split {s}", o_cat[row][None], lse_cat[row][None], o0[None],
+                           lse0[None], o_tol, LSE_TOL)
+
+
+def check_merged(run, ref, tokens, o_tol):
+    toks = np.asarray(sorted(set(int(t) for t in tokens)))
+    o = on.bf16_to_f64(host_bits(run.bufs.o))[toks]
+    lse = run.bufs.lse.cpu().numpy()[toks]
+    hp.compare(f"workload {run.w.cfg} merged over splits", o, lse, np.stack([ref[g][2] for g in toks]),
+               np.stack([ref[g][3] for g in toks]), o_tol, LSE_TOL)
+
+
+SPLIT_DENSE = {
+    # seed: (q_lens, kv_lens, P, H, kv_splits)
+    301: ([700, 1, 130], [700, 3000, 900], 2, 16, 3),  # prefill, a long decode row, a continuation
+    302: ([2048], [2048], 4, 16, 2),
+    303: ([64, 300, 1], [64, 300, 200], 1, 8, 5),       # more splits than some rows have tiles
+}
+
+
+@pytest.mark.parametrize("seed", sorted(SPLIT_DENSE))
+def test_split_kv_dense(gpu_lib, seed):
+    """Split-KV partials: each key range's partial matches the oracle on those keys, and the
+    merge of all (rank, split) partials with the sink once reproduces unsharded attention."""
+    q, kv, P, H, S = SPLIT_DENSE[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64)
+    run = DenseRun(w, kv_splits=S)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    check_merged(run, ref, toks, O_TOL)
+    pos, req = hp.token_maps(run.plan)
+    lat_all, rope_all = on.bf16_to_f64(run.lat_bits), on.bf16_to_f64(run.rope_bits)
+
+    def key_rows(g):
+        keys = np.arange(int(pos[g]) + 1)
+        rows = int(w.kv_start[req[g]]) + keys
+        return keys, lat_all[rows], rope_all[rows]
+    sample = hp.sample_tokens(w, run.plan, n_random=24)
+    check_split_partials(run, sample, key_rows, O_TOL)
+
+
+def test_split_kv_sparse(gpu_lib):
+    """Split-KV on the sparse fp8 path: per-split partials and the merge over splits."""
+    w = synth.custom(311, [900, 400], [900, 1300], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,
+                     kv_dtype="fp8", latent_std=1.0)
+    run = SparseRun(w, kv_splits=3)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_sparse(w, run.plan, run.q_bits, run.lat_codes, run.kv_scale, run.rope_bits, run.topk,
+                           run.sink, toks)
+    check_merged(run, ref, toks, SPARSE_O_TOL)
+    pos, req = hp.token_maps(run.plan)
+
+    def key_rows(g):
+        keys = oa.sparse_keyset(int(pos[g]), run.topk[g], w.window)
+        rows = int(w.kv_start[req[g]]) + keys
+        return keys, on.dequant_fp8_rows(run.lat_codes[rows], rows, run.kv_scale), on.bf16_to_f64(run.rope_bits[rows])
+    sample = hp.sample_tokens(w, run.plan, n_random=24)
+    check_split_partials(run, sample, key_rows, SPARSE_O_TOL)
 
 
 def test_sparse128k_p2_sampled(gpu_lib):

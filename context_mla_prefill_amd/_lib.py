@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_PKG, "libmla_pcp.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTED = ("mla_pcp_abi_version", "mla_pcp_last_error", "pcp_plan_sizes", "pcp_partition",
-            "pcp_kv_insert", "mla_prefill_partial", "pcp_lse_merge")
+            "pcp_kv_insert", "pcp_kv_insert_fp8", "mla_prefill_partial", "pcp_lse_merge")
 
 _lib = None
 
@@ -46,6 +46,7 @@ class mla_partial_args(ctypes.Structure):
         ("D_latent", _i32), ("D_rope", _i32), ("kv_dtype", _i32), ("N_kv", _i64),
         ("scale", ctypes.c_float), ("o_partial", _p), ("lse", _p),
         ("kv_splits", _i32), ("split_stride", _i64), ("vrow_kv_len", _p),
+        ("block_table", _p), ("bt_stride", _i32), ("vrow_req", _p),
     ]
 
 
@@ -65,10 +66,12 @@ def load():
     lib.pcp_plan_sizes.restype = ctypes.c_int
     lib.pcp_plan_sizes.argtypes = [_pi32, _pi32, _i32, _i32, _pi32, _pi32, _pi64]
     lib.pcp_partition.restype = ctypes.c_int
-    lib.pcp_partition.argtypes = [_p, _p, _p, _i32, _i32, _i64, _i32, _i64, _p, _p, _p, _p, _p, _p,
-                                  _p, _p, _p, _p]
+    lib.pcp_partition.argtypes = [_p, _p, _p, _i32, _i32, _i64, _i32, _i64, _p, _i32, _p, _p, _p, _p, _p,
+                                  _p, _p, _p, _p, _p]
     lib.pcp_kv_insert.restype = ctypes.c_int
     lib.pcp_kv_insert.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p, _p, _p]
+    lib.pcp_kv_insert_fp8.restype = ctypes.c_int
+    lib.pcp_kv_insert_fp8.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i64, _p, _p, _p, _p]
     lib.mla_prefill_partial.restype = ctypes.c_int
     lib.mla_prefill_partial.argtypes = [ctypes.POINTER(mla_partial_args), _p]
     lib.pcp_lse_merge.restype = ctypes.c_int
@@ -124,9 +127,10 @@ def pcp_plan_sizes(q_lens, kv_lens, P: int):
 
 def pcp_partition(q_lens, kv_lens, kv_start, P, T_glob, n_vrows, T_loc_total, cu_seqlens_glob,
                   cu_seqlens_q, vrow_req, vrow_kv_start, vrow_kv_len, local_gidx, positions, slot,
-                  merge_src, stream=None):
+                  merge_src, stream=None, block_table=None, bt_stride=0):
     st = load().pcp_partition(_ptr(q_lens), _ptr(kv_lens), _ptr(kv_start), int(q_lens.numel()), P,
-                              T_glob, n_vrows, T_loc_total, _ptr(cu_seqlens_glob), _ptr(cu_seqlens_q),
+                              T_glob, n_vrows, T_loc_total, _ptr(block_table), bt_stride,
+                              _ptr(cu_seqlens_glob), _ptr(cu_seqlens_q),
                               _ptr(vrow_req), _ptr(vrow_kv_start), _ptr(vrow_kv_len), _ptr(local_gidx),
                               _ptr(positions), _ptr(slot), _ptr(merge_src), _stream(stream))
     _check(st, "pcp_partition")
@@ -139,17 +143,25 @@ def pcp_kv_insert(local_latent, local_rope, slot, T_loc, D_latent, D_rope, kv_dt
     _check(st, "pcp_kv_insert")
 
 
+def pcp_kv_insert_fp8(local_latent, local_rope, slot, T, D_latent, D_rope, N_kv, kv_latent, kv_rope, kv_scale,
+                      stream=None):
+    st = load().pcp_kv_insert_fp8(_ptr(local_latent), _ptr(local_rope), _ptr(slot), T, D_latent, D_rope, N_kv,
+                                  _ptr(kv_latent), _ptr(kv_rope), _ptr(kv_scale), _stream(stream))
+    _check(st, "pcp_kv_insert_fp8")
+
+
 def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positions, n_vrows, T_loc, H,
                       D_latent, D_rope, scale, o_partial, lse, N_kv, kv_dtype=MLA_KV_BF16, kv_scale=None,
                       topk_idx=None, topk=0, window=0, kv_splits=1, split_stride=0,
-                      vrow_kv_len=None) -> mla_partial_args:
+                      vrow_kv_len=None, block_table=None, bt_stride=0, vrow_req=None) -> mla_partial_args:
     return mla_partial_args(
         q=_ptr(q), latent_kv=_ptr(latent_kv), kv_scale=_ptr(kv_scale), rope_k=_ptr(rope_k),
         cu_seqlens_q=_ptr(cu_seqlens_q), vrow_kv_start=_ptr(vrow_kv_start), positions=_ptr(positions),
         topk_idx=_ptr(topk_idx), topk=topk, window=window, n_vrows=n_vrows, T_loc=T_loc, H=H,
         D_latent=D_latent, D_rope=D_rope, kv_dtype=kv_dtype, N_kv=N_kv, scale=float(scale),
         o_partial=_ptr(o_partial), lse=_ptr(lse), kv_splits=kv_splits, split_stride=split_stride,
-        vrow_kv_len=_ptr(vrow_kv_len))
+        vrow_kv_len=_ptr(vrow_kv_len), block_table=_ptr(block_table), bt_stride=bt_stride,
+        vrow_req=_ptr(vrow_req))
 
 
 def mla_prefill_partial(args: mla_partial_args, stream=None):

@@ -76,7 +76,8 @@ mla_status pcp_plan_sizes(const int32_t* q_lens, const int32_t* kv_lens, int32_t
 
 mla_status pcp_partition(const int32_t* q_lens, const int32_t* kv_lens, const int32_t* kv_start,
                          int32_t n_req, int32_t P, int64_t T_glob, int32_t n_vrows,
-                         int64_t T_loc_total, int32_t* cu_seqlens_glob, int32_t* cu_seqlens_q,
+                         int64_t T_loc_total, const int32_t* block_table, int32_t bt_stride,
+                         int32_t* cu_seqlens_glob, int32_t* cu_seqlens_q,
                          int32_t* vrow_req, int32_t* vrow_kv_start, int32_t* vrow_kv_len,
                          int32_t* local_gidx, int32_t* positions, int32_t* slot,
                          int32_t* merge_src, void* stream) {
@@ -93,8 +94,9 @@ mla_status pcp_partition(const int32_t* q_lens, const int32_t* kv_lens, const in
     if (T_loc_total > 0 && (!local_gidx || !positions || !slot))
         return fail(MLA_ERR_INVALID_ARG, "pcp_partition: null per-row output");
     if (T_glob > 0 && !merge_src) return fail(MLA_ERR_INVALID_ARG, "pcp_partition: null merge_src");
+    if (block_table && bt_stride < 1) return fail(MLA_ERR_INVALID_ARG, "pcp_partition: bt_stride < 1");
     hipError_t e = launch_partition(q_lens, kv_lens, kv_start, n_req, P, T_glob, n_vrows, T_loc_total,
-                                    cu_seqlens_glob, cu_seqlens_q, vrow_req, vrow_kv_start, vrow_kv_len,
+                                    block_table, bt_stride, cu_seqlens_glob, cu_seqlens_q, vrow_req, vrow_kv_start, vrow_kv_len,
                                     local_gidx, positions, slot, merge_src, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "pcp_partition: %s", hipGetErrorString(e));
     return MLA_OK;
@@ -117,6 +119,23 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
     hipError_t e = launch_kv_insert(local_latent, local_rope, slot, T_loc, lb, rb, N_kv, kv_latent,
                                     kv_rope, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "pcp_kv_insert: %s", hipGetErrorString(e));
+    return MLA_OK;
+}
+
+mla_status pcp_kv_insert_fp8(const void* local_latent, const void* local_rope, const int32_t* slot,
+                             int32_t T, int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent,
+                             void* kv_rope, float* kv_scale, void* stream) {
+    if (T < 0 || N_kv < 0 || N_kv > INT32_MAX) return fail(MLA_ERR_INVALID_ARG, "pcp_kv_insert_fp8: sizes out of range");
+    if (!((D_latent == 512 && D_rope == 64) || (D_latent == 64 && D_rope == 16)))
+        return fail(MLA_ERR_UNSUPPORTED, "pcp_kv_insert_fp8: dims %d+%d unsupported", D_latent, D_rope);
+    if (T == 0) return MLA_OK;
+    if (!local_latent || !local_rope || !slot || !kv_latent || !kv_rope || !kv_scale)
+        return fail(MLA_ERR_INVALID_ARG, "pcp_kv_insert_fp8: null pointer");
+    if (!aligned16(local_latent) || !aligned16(local_rope) || !aligned16(kv_latent) || !aligned16(kv_rope))
+        return fail(MLA_ERR_INVALID_ARG, "pcp_kv_insert_fp8: buffers must be 16-byte aligned");
+    hipError_t e = launch_kv_insert_fp8(local_latent, local_rope, slot, T, D_latent, D_rope, N_kv, kv_latent, kv_rope,
+                                        kv_scale, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "pcp_kv_insert_fp8: %s", hipGetErrorString(e));
     return MLA_OK;
 }
 
@@ -163,6 +182,8 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
                                          "vrow_kv_len and outputs within int32 rows*H");
     if ((((int64_t)a->T_loc * a->H + 63) / 64 + a->n_vrows) * a->kv_splits > INT32_MAX)
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: too many workgroups");
+    if (a->block_table && (!a->vrow_req || a->bt_stride < 1))
+        return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: block_table needs vrow_req and bt_stride >= 1");
     if (a->T_loc == 0) return MLA_OK;
     if (!a->q || !a->latent_kv || !a->rope_k || !a->cu_seqlens_q || !a->vrow_kv_start ||
         !a->positions || !a->o_partial || !a->lse)

@@ -130,15 +130,19 @@ __device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ 
 // rows of this request's extent. Buffer loads rather than global ones: the compiler counts
 // a global (flat-family) load into LDS as an LDS access of unknown order and would then
 // wait for all LDS reads at once instead of keeping the Q K^T reads in flight.
+// Where the keys of one tile live: KV row of its first key and how many keys it has.
+struct TileRows {
+    int64_t row0;
+    int rows;  // 1..BN
+};
+
 template <class T, int DL, int DR>
 struct WideTile {
     __amdgpu_buffer_rsrc_t lat_rsrc, rope_rsrc;
     int rows;  // valid rows from the base, 1..BN
-    __device__ __forceinline__ WideTile(const char* lat, const char* rope, int64_t kv0, int kt, int64_t last) {
-        const int64_t tb = min((int64_t)kt * BN, last);
-        rows = (int)min((int64_t)BN, last - tb + 1);
-        lat_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(lat + (kv0 + tb) * (DL * 2)), 0, rows * (DL * 2), kBufferFlags);
-        rope_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rope + (kv0 + tb) * (DR * 2)), 0, rows * (DR * 2), kBufferFlags);
+    __device__ __forceinline__ WideTile(const char* lat, const char* rope, TileRows tr) : rows(tr.rows) {
+        lat_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(lat + tr.row0 * (DL * 2)), 0, rows * (DL * 2), kBufferFlags);
+        rope_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rope + tr.row0 * (DR * 2)), 0, rows * (DR * 2), kBufferFlags);
     }
     // Latent load i (0..15) of this wave: tile row n = 4 i + wave, one 1024-byte row per
     // load (row offset in an SGPR, lane offset constant). Rows past the extent repeat the
@@ -159,12 +163,11 @@ struct WideTile {
     }
 };
 
-// Other shapes: every load of tile kt, lanes that would land on a pad switched off.
-// Wave w issues loads w, w+4, ...
+// Other shapes: every load of a tile, lanes that would land on a pad switched off. Keys
+// past the tile's extent repeat its last key. Wave w issues loads w, w+4, ...
 template <class T, int DL, int DR>
 __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restrict__ lat,
-                                                 const char* __restrict__ rope, int64_t kv0, int kt,
-                                                 int64_t last, int wave, int lane) {
+                                                 const char* __restrict__ rope, TileRows tr, int wave, int lane) {
     constexpr int LV = T::LAT_VECS + 1, RV = T::ROPE_VECS + 1;
     const int lk = lane / LV;
     const int lc = lane - lk * LV;
@@ -177,29 +180,30 @@ __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restri
         const int n = i * 4 + wave;
         if (n >= T::LAT_LOADS) break;
         const int r = n * T::LAT_ROWS_PER_LOAD + lk;
-        const int64_t j = min((int64_t)kt * BN + r, last);
+        const int64_t j = tr.row0 + min(r, tr.rows - 1);
         if (lon && r < BN)
-            lds_dma16(lat + (kv0 + j) * (DL * 2) + lc * 16, dst + n * T::LAT_ROWS_PER_LOAD * T::LAT_STRIDE);
+            lds_dma16(lat + j * (DL * 2) + lc * 16, dst + n * T::LAT_ROWS_PER_LOAD * T::LAT_STRIDE);
     }
 #pragma unroll
     for (int i = 0; i < (T::ROPE_LOADS + 3) / 4; ++i) {
         const int n = i * 4 + ((wave + 2) & 3);
         if (n >= T::ROPE_LOADS) break;
         const int r = n * T::ROPE_ROWS_PER_LOAD + rk;
-        const int64_t j = min((int64_t)kt * BN + r, last);
+        const int64_t j = tr.row0 + min(r, tr.rows - 1);
         if (ron && r < BN)
-            lds_dma16(rope + (kv0 + j) * (DR * 2) + rc * 16,
+            lds_dma16(rope + j * (DR * 2) + rc * 16,
                       dst + T::ROPE_OFF + n * T::ROPE_ROWS_PER_LOAD * T::ROPE_STRIDE);
     }
 }
 
-template <int DL, int DR>
+template <int DL, int DR, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ lat, const char* __restrict__ rope,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out, int kv_splits, int64_t split_stride,
-    const int32_t* __restrict__ vrow_kv_len) {
+    const int32_t* __restrict__ vrow_kv_len, const int32_t* __restrict__ block_table, int bt_stride,
+    const int32_t* __restrict__ vrow_req) {
     using T = DenseTile<DL, DR>;
     __shared__ __attribute__((aligned(1024))) char kv_lds0[T::TILE_BYTES];  // KV tile double buffer:
     __shared__ __attribute__((aligned(1024))) char kv_lds1[T::TILE_BYTES];  // two separate objects
@@ -257,8 +261,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     int key_lo = 0;
     if (kv_splits > 1) {
         const int n = (vrow_kv_len[v] + BN - 1) / BN;
-        key_lo = BN * (int)(((int64_t)split * n) / kv_splits);
-        kv_hi = min(kv_hi, BN * (int)(((int64_t)(split + 1) * n) / kv_splits));
+        key_lo = BN * (int)((unsigned)split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
+        kv_hi = min(kv_hi, BN * (int)((unsigned)(split + 1) * n / kv_splits));
         o_out += split * split_stride * H * DL;
         lse_out += split * split_stride * H;
     }
@@ -269,7 +273,31 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) pmin = min(pmin, __shfl_xor(pmin, off));
     pmin = __builtin_amdgcn_readfirstlane(pmin);
-    const int64_t last = min((int64_t)kv_hi - 1, N_kv - 1 - kv0);  // last key row that may be read
+    // last key (request-relative) a load may touch
+    const int64_t last = PAGED ? (int64_t)kv_hi - 1 : min((int64_t)kv_hi - 1, N_kv - 1 - kv0);
+    // Paged KV: block ids of 64 consecutive tiles [bw_base, bw_base + 64), one per lane,
+    // read by v_readlane; the next 64 are fetched one tile before they are needed.
+    const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[v] * bt_stride : nullptr;
+    const int nblk = (int)(last >> 6) + 1;
+    int bw_base = 0, bw_v = 0;
+    auto bw_load = [&](int base) {
+        bw_base = base;
+        bw_v = bt_row[min(base + lane, nblk - 1)];
+    };
+    // KV rows of tile kt (request-relative keys clamped to `last`).
+    auto tile_rows = [&](int kt) -> TileRows {
+        const int64_t tb = min((int64_t)kt * BN, last);
+        TileRows tr;
+        tr.rows = (int)min((int64_t)BN, last - tb + 1);
+        if constexpr (PAGED) {
+            const int t = (int)(tb >> 6);
+            tr.row0 = (int64_t)__builtin_amdgcn_readlane(bw_v, t - bw_base) * 64 + (tb & 63);
+            if (t == bw_base + 63) bw_load(bw_base + 64);
+        } else {
+            tr.row0 = kv0 + tb;
+        }
+        return tr;
+    };
 
     constexpr int NB0 = T::NB / 2;  // O column blocks per wave
     f32x16 acc_o[NB0];
@@ -306,8 +334,9 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         for (int kb = 0; kb < T::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
         __syncthreads();                     // ... and every wave's; the other buffer is free
+        const TileRows next_rows = tile_rows(kt + 1);  // clamped past the last tile
         if constexpr (!T::WIDE) {
-            if (kt + 1 < n_tiles) narrow_load_tile<T, DL, DR>(nxt, lat, rope, kv0, kt + 1, last, wave, lane);
+            if (kt + 1 < n_tiles) narrow_load_tile<T, DL, DR>(nxt, lat, rope, next_rows, wave, lane);
         }
         // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
         f32x16 s = f32x16{};
@@ -315,7 +344,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
             const char* kl = kvt + k_lat_off;
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (T::WIDE) {
-                const WideTile<T, DL, DR> src(lat, rope, kv0, kt + 1, last);
+                const WideTile<T, DL, DR> src(lat, rope, next_rows);
 #pragma unroll
                 for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(nxt, wave, lane, i);
             }
@@ -341,7 +370,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (T::WIDE) {
-            const WideTile<T, DL, DR> src(lat, rope, kv0, kt + 1, last);
+            const WideTile<T, DL, DR> src(lat, rope, next_rows);
 #pragma unroll
             for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(nxt, wave, lane, u);
         }
@@ -441,14 +470,16 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     };
 
     if (kt0 < n_tiles) {  // workgroup-uniform; an empty key range leaves O = 0, LSE = -inf
+        if constexpr (PAGED) bw_load(min(kt0, nblk - 1) & ~63);
+        const TileRows first_rows = tile_rows(kt0);
         if constexpr (T::WIDE) {
-            const WideTile<T, DL, DR> src(lat, rope, kv0, kt0, last);
+            const WideTile<T, DL, DR> src(lat, rope, first_rows);
 #pragma unroll
             for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(kv_lds0, wave, lane, i);
 #pragma unroll
             for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(kv_lds0, wave, lane, u);
         } else {
-            narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, kv0, kt0, last, wave, lane);
+            narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, first_rows, wave, lane);
         }
         for (int kt = kt0; kt < n_tiles; kt += 2) {
             tile_step(kv_lds0, kv_lds1, kt);
@@ -482,21 +513,26 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     }
 }
 
-template <int DL, int DR>
+template <int DL, int DR, bool PAGED>
 hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
     const int64_t grid = (((int64_t)a.T_loc * a.H + BM - 1) / BM + a.n_vrows) * a.kv_splits;
-    hipLaunchKernelGGL((dense_partial_kernel<DL, DR>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((dense_partial_kernel<DL, DR, PAGED>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.n_vrows, a.H, a.N_kv, a.scale * kLog2e,
-                       (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len);
+                       (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len, a.block_table,
+                       a.bt_stride, a.vrow_req);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream) {
-    if (a.D_latent == 512) return launch_dense<512, 64>(a, stream);
-    return launch_dense<64, 16>(a, stream);
+    if (a.block_table) {
+        if (a.D_latent == 512) return launch_dense<512, 64, true>(a, stream);
+        return launch_dense<64, 16, true>(a, stream);
+    }
+    if (a.D_latent == 512) return launch_dense<512, 64, false>(a, stream);
+    return launch_dense<64, 16, false>(a, stream);
 }
 
 }  // namespace mla

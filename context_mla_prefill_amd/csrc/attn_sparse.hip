@@ -32,6 +32,7 @@ namespace {
 using namespace attn;
 
 constexpr int MAX_TOPK = 2048;
+constexpr int MAX_WINDOW = 4096;
 constexpr int GATHER_LOADS = BN / 2 / 4 + 1;  // per wave and tile: latent loads (2 keys each) + 1 scale load
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -46,20 +47,22 @@ __device__ __forceinline__ void dequant4(uint32_t w, float sc, __bf16* out) {
     out[3] = (__bf16)(b.y * sc);
 }
 
-template <int DL, int DR>
+template <int DL, int DR, bool PAGED>
 __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const __bf16* __restrict__ q, const uint8_t* __restrict__ lat8, const float* __restrict__ kv_scale,
     const char* __restrict__ rope, const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start,
     const int32_t* __restrict__ positions, const int32_t* __restrict__ topk_idx, int topk, int window,
     int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out,
-    int kv_splits, int64_t split_stride, const int32_t* __restrict__ vrow_kv_len) {
+    int kv_splits, int64_t split_stride, const int32_t* __restrict__ vrow_kv_len,
+    const int32_t* __restrict__ block_table, int bt_stride, const int32_t* __restrict__ vrow_req) {
     using S = Shape<DL, DR>;
     static_assert(DL == 512, "the fp8 staging assumes 512-byte latent rows");
     __shared__ __attribute__((aligned(1024))) char kv_lat[S::ROPE_OFF];        // bf16 latent rows of the current tile
     __shared__ __attribute__((aligned(16))) char kv_rope[BN * S::ROPE_STRIDE];  // and their rope rows
     __shared__ __attribute__((aligned(1024))) uint8_t stage[2][BN * DL];    // fp8 rows of the next two tiles
     __shared__ float stage_scale[2][BN];
-    __shared__ int sel[MAX_TOPK];            // this token's selected indices
+    __shared__ int sel[MAX_TOPK];            // KV row of each selected key of the set, -1 otherwise
+    __shared__ int win_blk[MAX_WINDOW / BN + 1];  // paged: cache blocks the window spans
     __shared__ uint64_t tmask[2];            // valid-key bits per staging slot
     __shared__ Exchange ex;
 
@@ -89,24 +92,44 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     int key_lo = 0, key_hi = INT32_MAX;
     if (kv_splits > 1) {
         const int n = (vrow_kv_len[lo_v] + BN - 1) / BN;
-        key_lo = BN * (int)(((int64_t)split * n) / kv_splits);
-        key_hi = BN * (int)(((int64_t)(split + 1) * n) / kv_splits);
+        key_lo = BN * (int)((unsigned)split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
+        key_hi = BN * (int)((unsigned)(split + 1) * n / kv_splits);
         o_out += split * split_stride * H * DL;
         lse_out += split * split_stride * H;
     }
     const int head = hg * BM + pair * 32 + l32;
     const int64_t grow = (int64_t)tok * H + head;
-    // Buffer views (keys are request-relative): fp8 latent rows of DL bytes, bf16 rope rows,
-    // and the 64-row scales of the whole cache. The caller keeps N_kv * DL below 2^32.
-    const int last_key = (int)(N_kv - 1 - kv0);
+    // Keys are addressed by row relative to row_base: the request's first row for packed KV
+    // (row = key position), 0 for paged KV (row = block_table entry * 64 + position % 64).
+    // Buffer views: fp8 latent rows of DL bytes, bf16 rope rows, and the 64-row scales of
+    // the whole cache. The caller keeps N_kv * DL below 2^32.
+    const int64_t row_base = PAGED ? 0 : kv0;
+    const int last_row = (int)(N_kv - 1 - row_base);
     const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(lat8 + kv0 * DL), 0, (int)(uint32_t)((N_kv - kv0) * DL), kBufferFlags);
+        (void*)(lat8 + row_base * DL), 0, (int)(uint32_t)((N_kv - row_base) * DL), kBufferFlags);
     const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(rope + kv0 * (DR * 2)), 0, (int)(uint32_t)((N_kv - kv0) * (DR * 2)), kBufferFlags);
+        (void*)(rope + row_base * (DR * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DR * 2)), kBufferFlags);
     const __amdgpu_buffer_rsrc_t scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)kv_scale, 0, (int)(uint32_t)(((N_kv + 63) / 64) * 4), kBufferFlags);
+    const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[lo_v] * bt_stride : nullptr;
+    // Empty slots read the row of key 0 (a written key of the request: its value meets a
+    // zero probability, so it must be finite).
+    const int pad_row = PAGED ? bt_row[0] * BN : 0;
+    const int win_lo = max(0, p - window + 1);  // first window key (window > 0)
 
-    for (int i = tid; i < MAX_TOPK; i += NT) sel[i] = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
+    // The selected indices, filtered once: an entry outside [0, p], outside this split's key
+    // range or inside the window (which supplies it) becomes -1; a kept one becomes its row.
+    for (int i = tid; i < MAX_TOPK; i += NT) {
+        const int e = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
+        const bool ok = e >= key_lo && e < key_hi && e <= p && (window == 0 || e < win_lo);
+        int r = -1;
+        if (ok) r = PAGED ? bt_row[e >> 6] * BN + (e & (BN - 1)) : e;
+        sel[i] = r;
+    }
+    if constexpr (PAGED) {
+        const int nwb = window > 0 ? (p >> 6) - (win_lo >> 6) + 1 : 0;  // <= MAX_WINDOW / BN + 1
+        for (int i = tid; i < nwb; i += NT) win_blk[i] = bt_row[(win_lo >> 6) + i];
+    }
 
     bf16x8 qf[S::KB];
     {
@@ -116,22 +139,22 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     }
     __syncthreads();
 
-    const int win_lo = max(0, p - window + 1);  // first window key (window > 0)
     const int n_sel_tiles = (topk + BN - 1) / BN;
     const int n_tiles = n_sel_tiles + (window + BN - 1) / BN;
 
-    // Key of slot j of tile t (request-relative) and whether the slot holds a key of the set;
-    // tiles past the last one hold no key (their slots read key 0).
+    // Row (relative to row_base) of the key in slot j of tile t and whether the slot holds a
+    // key of the set; empty slots and tiles past the last one read pad_row.
     auto slot_key = [&](int t, int j, bool& ok) -> int {
         if (t < n_sel_tiles) {
             const int e = sel[t * BN + j];
-            ok = e >= key_lo && e < key_hi && e <= p && (window == 0 || e < win_lo);
-            return ok ? e : 0;
+            ok = e >= 0;
+            return ok ? e : pad_row;
         }
         const int w = (t - n_sel_tiles) * BN + j;
         const int k = win_lo + w;
         ok = window > 0 && w < window && k <= p && k >= key_lo && k < key_hi;
-        return ok ? k : 0;
+        if (!ok) return pad_row;
+        return PAGED ? win_blk[(k >> 6) - (win_lo >> 6)] * BN + (k & (BN - 1)) : k;
     };
     // Next tile index >= t that holds at least one key (n_tiles if none); workgroup-uniform.
     auto next_live = [&](int t) -> int {
@@ -150,15 +173,15 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         for (int i = 0; i < BN / 2 / 4; ++i) {
             const int n = i * 4 + wave;
             bool ok;
-            const int key = min(slot_key(t, 2 * n + half, ok), last_key);
+            const int key = min(slot_key(t, 2 * n + half, ok), last_row);
             lds_dma16(lat_rsrc, (uint32_t)key * DL + l32 * 16, (char*)stage[b] + n * 1024);
         }
         {
             bool ok;
-            const int key = min(slot_key(t, 16 * wave + (lane & 15), ok), last_key);
+            const int key = min(slot_key(t, 16 * wave + (lane & 15), ok), last_row);
             if (lane < 16)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(scale_rsrc, (lds_void*)&stage_scale[b][16 * wave], 4,
-                                                         (uint32_t)((kv0 + key) >> 6) * 4, 0, 0, 0);
+                                                         (uint32_t)((row_base + key) >> 6) * 4, 0, 0, 0);
         }
         if (wave == 0) {
             bool ok;
@@ -179,7 +202,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
             if (n >= S::ROPE_LOADS) break;  // wave-uniform
             const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
             bool ok;
-            const int key = min(slot_key(t, r < BN ? r : 0, ok), last_key);
+            const int key = min(slot_key(t, r < BN ? r : 0, ok), last_row);
             if (ron && r < BN)
                 lds_dma16(rope_rsrc, (uint32_t)key * (DR * 2) + rc * 16, kv_rope + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
         }
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         tn = next_live(t + 1);
         gather_latent(t, 0);
         gather_rope(t);
-        gather_latent(tn, 1);  // tn may be past the last tile: loads of key 0, never used
+        gather_latent(tn, 1);  // tn may be past the last tile: loads of pad_row, never used
     }
     while (t < n_tiles) {
 #pragma unroll
@@ -257,16 +280,21 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     write_rows<S, DL>(acc_o, m_ref, l_run, true, grow, wave, side, lane, ex, o_out, lse_out);
 }
 
-}  // namespace
-
-hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream) {
+template <bool PAGED>
+hipError_t launch_sparse(const mla_partial_args& a, hipStream_t stream) {
     const int64_t grid = (int64_t)a.T_loc * (a.H / BM) * a.kv_splits;
-    hipLaunchKernelGGL((sparse_partial_kernel<512, 64>), dim3((unsigned)grid), dim3(NT), 0, stream,
+    hipLaunchKernelGGL((sparse_partial_kernel<512, 64, PAGED>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const uint8_t*)a.latent_kv, a.kv_scale, (const char*)a.rope_k,
                        a.cu_seqlens_q, a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H,
                        a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride,
-                       a.vrow_kv_len);
+                       a.vrow_kv_len, a.block_table, a.bt_stride, a.vrow_req);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream) {
+    return a.block_table ? launch_sparse<true>(a, stream) : launch_sparse<false>(a, stream);
 }
 
 }  // namespace mla

@@ -5,10 +5,14 @@
 //
 // One thread moves one 16-byte vector; a row's latent and rope vectors are handled by
 // consecutive threads so global reads and writes stay coalesced.
+#include <math.h>
+
 #include "internal.h"
 
 namespace mla {
 namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(256) void kv_insert_kernel(
     const uint4* __restrict__ lat_src, const uint4* __restrict__ rope_src,
@@ -29,7 +33,105 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Quantise-on-insert into an fp8-e4m3 cache with one fp32 scale per 64-row block
+// ("[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch Arguments": fp8 MLA KV
+// cache, block size 64). A block is opened by the call that writes its first row: that
+// call sets its scale from the rows it writes there; rows written into a block that an
+// earlier call opened use the stored scale. Three launches in stream order:
+//   1. the scale word of every block opened here is set to "amax 0, pending" (bit 31 marks
+//      a word that still holds an amax rather than a scale; scales are positive, bit 31
+//      clear);
+//   2. one wave per row folds the row's max |x| into its block word with an atomic max
+//      when that word is pending (non-negative fp32 bits order like their values);
+//   3. one wave per row turns a pending word into the scale amax / 448 (1 when amax is 0)
+//      -- every row of a block computes the same value, so racing writers agree -- then
+//      writes its codes e4m3fn_rne(clamp(x / scale, -448, 448)) and copies its rope row.
+constexpr uint32_t kPending = 0x80000000u;
+
+__global__ __launch_bounds__(256) void fp8_block_reset(const int32_t* __restrict__ slot, int T, int64_t N_kv,
+                                                       uint32_t* __restrict__ scale_word) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T) return;
+    const int64_t s = slot[i];
+    if (s >= 0 && s < N_kv && (s & 63) == 0) scale_word[s >> 6] = kPending;
+}
+
+template <int DL>
+__global__ __launch_bounds__(256) void fp8_block_amax(const __bf16* __restrict__ lat, const int32_t* __restrict__ slot,
+                                                      int T, int64_t N_kv, uint32_t* __restrict__ scale_word) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= T) return;  // wave-uniform
+    const int64_t s = slot[row];
+    if (s < 0 || s >= N_kv) return;
+    float a = 0.0f;
+    for (int e = 8 * lane; e < DL; e += 512) {  // 8 elements (16 bytes) per lane
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(lat + (int64_t)row * DL + e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf((float)x[k]));
+    }
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    // pending-ness is fixed for the whole launch: set by the previous one, cleared by the next
+    if (lane == 0 && (scale_word[s >> 6] & kPending)) atomicMax(scale_word + (s >> 6), kPending | __float_as_uint(a));
+}
+
+template <int DL, int DR>
+__global__ __launch_bounds__(256) void fp8_quantize_rows(const __bf16* __restrict__ lat, const __bf16* __restrict__ rope,
+                                                         const int32_t* __restrict__ slot, int T, int64_t N_kv,
+                                                         uint8_t* __restrict__ lat_dst, __bf16* __restrict__ rope_dst,
+                                                         uint32_t* __restrict__ scale_word) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= T) return;  // wave-uniform
+    const int64_t s = slot[row];
+    if (s < 0 || s >= N_kv) return;
+    const uint32_t w = scale_word[s >> 6];
+    float sc;
+    if (w & kPending) {
+        const float a = __uint_as_float(w & ~kPending);
+        sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+        if (lane == 0) scale_word[s >> 6] = __float_as_uint(sc);
+    } else {
+        sc = __uint_as_float(w);
+    }
+    for (int e = 8 * lane; e < DL; e += 512) {  // 8 elements in, 8 codes out per lane
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(lat + (int64_t)row * DL + e);
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = fminf(fmaxf(__fdiv_rn((float)x[k], sc), -448.0f), 448.0f);
+        // OCP E4M3FN codes, round to nearest even; bytes k of the word are elements k
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+        *reinterpret_cast<uint2*>(lat_dst + s * DL + e) = make_uint2((uint32_t)lo, (uint32_t)hi);
+    }
+    for (int e = lane; e < DR; e += 64) rope_dst[s * DR + e] = rope[(int64_t)row * DR + e];
+}
+
+template <int DL, int DR>
+hipError_t launch_fp8_insert(const void* local_latent, const void* local_rope, const int32_t* slot, int32_t T,
+                             int64_t N_kv, void* kv_latent, void* kv_rope, float* kv_scale, hipStream_t stream) {
+    uint32_t* words = reinterpret_cast<uint32_t*>(kv_scale);
+    hipLaunchKernelGGL(fp8_block_reset, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream, slot, T, N_kv, words);
+    hipLaunchKernelGGL((fp8_block_amax<DL>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
+                       (const __bf16*)local_latent, slot, T, N_kv, words);
+    hipLaunchKernelGGL((fp8_quantize_rows<DL, DR>), dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
+                       (const __bf16*)local_latent, (const __bf16*)local_rope, slot, T, N_kv, (uint8_t*)kv_latent,
+                       (__bf16*)kv_rope, words);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_kv_insert_fp8(const void* local_latent, const void* local_rope, const int32_t* slot, int32_t T,
+                                int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent, void* kv_rope,
+                                float* kv_scale, hipStream_t stream) {
+    if (D_latent == 512)
+        return launch_fp8_insert<512, 64>(local_latent, local_rope, slot, T, N_kv, kv_latent, kv_rope, kv_scale, stream);
+    return launch_fp8_insert<64, 16>(local_latent, local_rope, slot, T, N_kv, kv_latent, kv_rope, kv_scale, stream);
+}
 
 hipError_t launch_kv_insert(const void* local_latent, const void* local_rope, const int32_t* slot,
                             int32_t T_loc, int32_t latent_bytes, int32_t rope_bytes, int64_t N_kv,

@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kScanThreads) void plan_vrows(
 __global__ __launch_bounds__(256) void plan_tokens(
     const int32_t* __restrict__ q_lens, const int32_t* __restrict__ kv_lens,
     const int32_t* __restrict__ kv_start, int n_req, int P, int T_glob, int n_vrows, int T_loc_total,
+    const int32_t* __restrict__ block_table, int bt_stride,
     const int32_t* __restrict__ cu_glob, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ vrow_req, int32_t* __restrict__ local_gidx,
     int32_t* __restrict__ positions, int32_t* __restrict__ slot, int32_t* __restrict__ merge_src) {
@@ -137,7 +138,10 @@ __global__ __launch_bounds__(256) void plan_tokens(
     const int i = t - cu_glob[b];
     const int q = q_lens[b], kv = kv_lens[b];
     const int pos = kv - q + i;
-    const int sl = kv_start[b] + pos;
+    // KV row of the token: packed after the request's first row, or through its block
+    // (64 rows) in the block table
+    const int sl = block_table ? block_table[(int64_t)b * bt_stride + (pos >> 6)] * 64 + (pos & 63)
+                               : kv_start[b] + pos;
     // first virtual row of request b: lower bound of b in rank 0's vrow_req
     int vlo = 0, vhi = n_vrows;
     while (vlo < vhi) {
@@ -188,7 +192,8 @@ __global__ __launch_bounds__(256) void plan_tokens(
 
 hipError_t launch_partition(const int32_t* q_lens, const int32_t* kv_lens, const int32_t* kv_start,
                             int32_t n_req, int32_t P, int64_t T_glob, int32_t n_vrows,
-                            int64_t T_loc_total, int32_t* cu_glob, int32_t* cu_q, int32_t* vrow_req,
+                            int64_t T_loc_total, const int32_t* block_table, int32_t bt_stride,
+                            int32_t* cu_glob, int32_t* cu_q, int32_t* vrow_req,
                             int32_t* vrow_kv_start, int32_t* vrow_kv_len, int32_t* local_gidx,
                             int32_t* positions, int32_t* slot, int32_t* merge_src,
                             hipStream_t stream) {
@@ -198,7 +203,8 @@ hipError_t launch_partition(const int32_t* q_lens, const int32_t* kv_lens, const
     if (e != hipSuccess || T_glob == 0) return e;
     const int blocks = (int)((T_glob + 255) / 256);
     hipLaunchKernelGGL(plan_tokens, dim3(blocks), dim3(256), 0, stream, q_lens, kv_lens, kv_start, n_req,
-                       P, (int)T_glob, n_vrows, (int)T_loc_total, cu_glob, cu_q, vrow_req, local_gidx,
+                       P, (int)T_glob, n_vrows, (int)T_loc_total, block_table, bt_stride, cu_glob, cu_q,
+                       vrow_req, local_gidx,
                        positions, slot, merge_src);
     return hipGetLastError();
 }

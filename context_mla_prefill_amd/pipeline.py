@@ -37,6 +37,7 @@ class DevicePlan:
     positions: torch.Tensor
     slot: torch.Tensor
     merge_src: torch.Tensor  # [T_glob, P]
+    block_table: torch.Tensor | None = None  # [n_req, bt_stride] 64-row cache blocks (paged KV)
 
     @property
     def T_total(self) -> int:
@@ -46,7 +47,9 @@ class DevicePlan:
         return slice(self.row_off[r], self.row_off[r] + self.T_loc[r])
 
 
-def alloc_plan(q_lens, kv_lens, kv_start, P: int, device="cuda") -> DevicePlan:
+def alloc_plan(q_lens, kv_lens, kv_start, P: int, device="cuda", block_table=None) -> DevicePlan:
+    """Plan buffers for the given lengths; ``block_table`` (host or device int32
+    [n_req, bt_stride]) switches the KV addressing to paged."""
     q_h = np.ascontiguousarray(q_lens, dtype=np.int32)
     kv_h = np.ascontiguousarray(kv_lens, dtype=np.int32)
     T_loc, n_vrows, T_glob = _lib.pcp_plan_sizes(q_h, kv_h, P)
@@ -62,13 +65,15 @@ def alloc_plan(q_lens, kv_lens, kv_start, P: int, device="cuda") -> DevicePlan:
         vrow_req=torch.empty(P, max(n_vrows, 0), **i32), vrow_kv_start=torch.empty(P, n_vrows, **i32),
         vrow_kv_len=torch.empty(P, n_vrows, **i32), local_gidx=torch.empty(tot, **i32),
         positions=torch.empty(tot, **i32), slot=torch.empty(tot, **i32),
-        merge_src=torch.empty(T_glob, P, **i32))
+        merge_src=torch.empty(T_glob, P, **i32),
+        block_table=None if block_table is None else torch.as_tensor(block_table, dtype=torch.int32).to(device))
 
 
 def run_partition(pl: DevicePlan, stream=None):
     _lib.pcp_partition(pl.q_lens, pl.kv_lens, pl.kv_start, pl.P, pl.T_glob, pl.n_vrows, pl.T_total,
                        pl.cu_glob, pl.cu_q, pl.vrow_req, pl.vrow_kv_start, pl.vrow_kv_len, pl.local_gidx,
-                       pl.positions, pl.slot, pl.merge_src, stream)
+                       pl.positions, pl.slot, pl.merge_src, stream, block_table=pl.block_table,
+                       bt_stride=0 if pl.block_table is None else int(pl.block_table.shape[1]))
 
 
 @dataclass
@@ -115,7 +120,9 @@ def partial_args(pl: DevicePlan, r: int, ri: RankInputs, kv_latent, kv_rope, buf
         scale=scale, o_partial=bufs.o_cat[rows], lse=bufs.lse_cat[rows], N_kv=int(kv_latent.shape[0]),
         kv_dtype=kv_dtype, kv_scale=kv_scale, topk_idx=ri.topk, topk=topk, window=window,
         kv_splits=kv_splits, split_stride=pl.T_total if kv_splits > 1 else 0,
-        vrow_kv_len=pl.vrow_kv_len[r] if kv_splits > 1 else None)
+        vrow_kv_len=pl.vrow_kv_len[r] if kv_splits > 1 else None, block_table=pl.block_table,
+        bt_stride=0 if pl.block_table is None else int(pl.block_table.shape[1]),
+        vrow_req=None if pl.block_table is None else pl.vrow_req[r])
 
 
 def run_merge(pl: DevicePlan, bufs: StepBuffers, sink, H: int, Dl: int, stream=None, kv_splits: int = 1):

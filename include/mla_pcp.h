@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define MLA_PCP_ABI_VERSION 2
+#define MLA_PCP_ABI_VERSION 3
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -77,6 +77,11 @@ mla_status pcp_plan_sizes(const int32_t* q_lens, const int32_t* kv_lens, int32_t
  * Inputs (device int32 [n_req]): q_lens, kv_lens, kv_start (first packed KV row of
  * each request). Sizes T_glob, n_vrows, T_loc_total (= sum of T_loc) must be the ones
  * pcp_plan_sizes returned for the same lengths.
+ * Paged KV (block_table != NULL): the cache is a pool of 64-row blocks and request b's
+ * key at position j lives in row block_table[b * bt_stride + j / 64] * 64 + j % 64
+ * ("[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch Arguments": KV cache
+ * block size 64); block_table is device int32 [n_req][bt_stride] with ceil(kv_len / 64)
+ * entries per request. kv_start is then only copied to vrow_kv_start.
  * Outputs (device int32), ranks concatenated in rank order; rank r's rows start at
  * row_off[r] = T_loc[0] + ... + T_loc[r-1]:
  *  cu_seqlens_glob [n_req+1]           global token offsets of the requests.
@@ -88,7 +93,8 @@ mla_status pcp_plan_sizes(const int32_t* q_lens, const int32_t* kv_lens, int32_t
  *  local_gidx      [T_loc_total]       global token of each local row.
  *  positions       [T_loc_total]       kv_len - q_len + (index of the token among the
  *                                      request's new tokens).
- *  slot            [T_loc_total]       kv_start + position (packed KV row).
+ *  slot            [T_loc_total]       KV row of the token: kv_start + position, or its
+ *                                      row through the block table.
  *  merge_src       [T_glob][P]         row (in the rank-concatenated buffers) that rank
  *                                      p contributes to global token t, else -1. Split
  *                                      tokens have one entry (their rank); replicated
@@ -99,7 +105,8 @@ mla_status pcp_plan_sizes(const int32_t* q_lens, const int32_t* kv_lens, int32_t
  */
 mla_status pcp_partition(const int32_t* q_lens, const int32_t* kv_lens, const int32_t* kv_start,
                          int32_t n_req, int32_t P, int64_t T_glob, int32_t n_vrows,
-                         int64_t T_loc_total, int32_t* cu_seqlens_glob, int32_t* cu_seqlens_q,
+                         int64_t T_loc_total, const int32_t* block_table, int32_t bt_stride,
+                         int32_t* cu_seqlens_glob, int32_t* cu_seqlens_q,
                          int32_t* vrow_req, int32_t* vrow_kv_start, int32_t* vrow_kv_len,
                          int32_t* local_gidx, int32_t* positions, int32_t* slot,
                          int32_t* merge_src, void* stream);
@@ -124,6 +131,33 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
                          int64_t N_kv, void* kv_latent, void* kv_rope, void* stream);
 
 /*
+ * pcp_kv_insert_fp8 — write bf16 latent rows into an fp8-e4m3 KV cache at their slots,
+ * quantising on insert, and their bf16 rope rows alongside. The cache keeps one fp32
+ * scale per 64-row block ("[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch
+ * Arguments": fp8 MLA KV cache, block size 64; the scale layout is this library's).
+ * A block B is opened by the call that writes its first row (slot % 64 == 0); for it
+ *   a = max |x| over the latent elements this call writes into B (as fp32),
+ *   kv_scale[B] = a / 448 (fp32 division; 1 when a == 0).
+ * A block opened by an earlier call keeps its scale (a chunked prefill that continues a
+ * block quantises against the scale its first chunk set). Every written element gets
+ *   code = e4m3fn_rne(clamp(x / kv_scale[B], -448, 448)) (fp32 division, round to
+ *   nearest even, saturating).
+ * Writing rows of a block whose first row was never written leaves them against an
+ * undefined scale. All-gathered rows go in one call (a block split across two ranks'
+ * chunks is then opened once). Calls that run concurrently on one cache race; two rows
+ * with the same slot race.
+ *  local_latent  device bf16 [T][D_latent]; local_rope device bf16 [T][D_rope].
+ *  slot          device int32 [T] destination rows; rows outside [0, N_kv) are skipped.
+ *  kv_latent     device uint8 [N_kv][D_latent] (written); kv_rope device bf16 [N_kv][D_rope];
+ *  kv_scale      device fp32 [ceil(N_kv / 64)] (the touched blocks' entries written).
+ * Errors: INVALID_ARG (null, T < 0, N_kv < 0, 16-byte misalignment); UNSUPPORTED (dims other
+ * than 512+64 / 64+16); HIP.
+ */
+mla_status pcp_kv_insert_fp8(const void* local_latent, const void* local_rope, const int32_t* slot,
+                             int32_t T, int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent,
+                             void* kv_rope, float* kv_scale, void* stream);
+
+/*
  * mla_prefill_partial — one rank's partial MLA attention against the full KV, without
  * the sink. Absorbed MLA: every query head attends one shared latent KV head, key =
  * latent || rope (D_latent + D_rope), value = latent (D_latent). Each PCP rank computes
@@ -133,13 +167,16 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
  * virtual-batch PCP for MLA", "DualChunkSwap partitioning").
  *
  * For local row i (virtual row v, position p = positions[i]) and head h:
- *   dense  (topk_idx == NULL): keys are KV rows vrow_kv_start[v] + j, j = 0..p;
+ *   dense  (topk_idx == NULL): keys are the request's positions j = 0..p, at KV rows
+ *          vrow_kv_start[v] + j, or through block_table as in pcp_partition (request
+ *          vrow_req[v]) when block_table != NULL;
  *   sparse (topk_idx != NULL): keys j in {topk_idx[i][*] in [0, p]} union
  *          [max(0, p-window+1), p], counted once (entries -1 or outside [0, p] are
  *          pads; order does not matter).
  *   S_j = scale * <q[i][h], key_j>; O = softmax(S) @ latent (bf16, round to nearest
  *   even); LSE = log(sum_j exp(S_j)) (fp32, natural log). No sink.
- * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]).
+ * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]) (row = KV row, so
+ *   with paging one scale per block).
  * Split KV (kv_splits = S > 1): the key set of a row is cut by key position into S
  *   ranges and each range gives its own partial (O, LSE), written at split slice s of
  *   the outputs; merging the S partials (pcp_lse_merge with the same S) gives the
@@ -177,10 +214,14 @@ typedef struct mla_partial_args {
                                     next (>= T_loc when kv_splits > 1)                    */
     const int32_t* vrow_kv_len;  /* device [n_vrows] last position of the virtual row + 1,
                                     as pcp_partition writes it (needed when kv_splits > 1) */
+    const int32_t* block_table;  /* device [n_req][bt_stride] or NULL (packed KV)          */
+    int32_t bt_stride;           /* entries per request row of block_table                 */
+    const int32_t* vrow_req;     /* device [n_vrows] request of each virtual row (paged)   */
 } mla_partial_args;
 
 /* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales,
- * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1);
+ * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1,
+ * block_table without vrow_req or with bt_stride < 1);
  * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
  * bf16 KV, with H not a multiple of 64 or with N_kv >= 2^23 rows, dense with fp8 KV,
  * dtype); HIP.

@@ -53,3 +53,32 @@ def dequant_fp8_rows(codes: np.ndarray, row_ids: np.ndarray, scales: np.ndarray)
     s = np.asarray(scales, dtype=np.float32)[np.asarray(row_ids) // 64]
     prod = (v * s[:, None]).astype(np.float32)  # one binary32 rounding
     return f32_to_bf16_rne(prod)
+
+
+def _e4m3fn_magnitudes() -> np.ndarray:
+    """Values of the finite non-negative codes 0x00..0x7E, in code order (increasing)."""
+    return e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3fn_encode_rne(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP E4M3FN code of each binary32 value in [-448, 448] (ties to the even
+    code, i.e. mantissa LSB 0); the sign bit follows the sign of x, -0.0 included.
+
+    The finite magnitudes are increasing in code order, so the nearest one is one of the
+    two that bracket |x|; of two at the same distance the even code wins (round to
+    nearest even). Values outside [-448, 448] or NaN are rejected: the caller clamps.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    if np.any(~(a <= 448.0)):
+        raise ValueError("e4m3fn_encode_rne takes finite values in [-448, 448]")
+    mags = _e4m3fn_magnitudes()
+    hi = np.searchsorted(mags, a, side="left")  # first magnitude >= |x|
+    hi = np.minimum(hi, len(mags) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(x)
+    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)

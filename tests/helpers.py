@@ -35,17 +35,22 @@ def oracle_dense(w, plan, q_bits, lat_bits, rope_bits, sink, tokens):
         scale=float(w.scale), sink=np.asarray(sink, dtype=np.float64))
 
 
-def oracle_sparse(w, plan, q_bits, lat_codes, kv_scale, rope_bits, topk_rows, sink, tokens):
-    """fp64 (O0, LSE0, O, LSE) per token for the top-k + window key set over fp8 latent."""
+def oracle_sparse(w, plan, q_bits, lat_codes, kv_scale, rope_bits, topk_rows, sink, tokens, rows_of=None):
+    """fp64 (O0, LSE0, O, LSE) per token for the top-k + window key set over fp8 latent.
+
+    ``rows_of(b, keys)`` gives the cache rows of request b's keys (default: the packed
+    rows kv_start[b] + keys); latent codes and scales are read at those rows, rope at the
+    packed rows of ``rope_bits``."""
     pos, req = token_maps(plan)
     out = {}
     for t in np.asarray(tokens, dtype=np.int64):
         b = int(req[t])
         p = int(pos[t])
         keys = oa.sparse_keyset(p, topk_rows[t], w.window)
-        rows = int(w.kv_start[b]) + keys
+        packed = int(w.kv_start[b]) + keys
+        rows = packed if rows_of is None else rows_of(b, keys)
         lat = on.dequant_fp8_rows(lat_codes[rows], rows, kv_scale)
-        rope = on.bf16_to_f64(rope_bits[rows])
+        rope = on.bf16_to_f64(rope_bits[packed])
         out[int(t)] = oa.attend_keyset(on.bf16_to_f64(q_bits[t]), lat, rope, float(w.scale),
                                        np.asarray(sink, dtype=np.float64))
     return out

@@ -112,6 +112,8 @@ def test_partial_validation_errors():
     assert call(_args(**ok, kv_splits=65))[0] == _lib.MLA_ERR_INVALID_ARG
     assert call(_args(**ok, kv_splits=2, split_stride=4))[0] == _lib.MLA_ERR_INVALID_ARG  # no vrow_kv_len
     assert call(_args(**ok, kv_splits=2, split_stride=3, vrow_kv_len=f))[0] == _lib.MLA_ERR_INVALID_ARG  # < T_loc
+    assert call(_args(**ok, block_table=f, bt_stride=4))[0] == _lib.MLA_ERR_INVALID_ARG  # no vrow_req
+    assert call(_args(**ok, block_table=f, bt_stride=0, vrow_req=f))[0] == _lib.MLA_ERR_INVALID_ARG
     st, msg = call(_args(**ok, D_rope=32))
     assert st == _lib.MLA_ERR_UNSUPPORTED and "dims" in msg
     # empty shard: nothing to do, OK without touching any pointer
@@ -139,6 +141,16 @@ def test_merge_and_insert_validation_errors():
     assert ins(slot=None)[0] == _lib.MLA_ERR_INVALID_ARG
     assert ins(T_loc=-2)[0] == _lib.MLA_ERR_INVALID_ARG
     assert ins(T_loc=0)[0] == 0
+    q8 = lambda **kw: _status(lambda: _lib.pcp_kv_insert_fp8(**{**dict(
+        local_latent=f, local_rope=f, slot=f, T=4, D_latent=512, D_rope=64, N_kv=128, kv_latent=f,
+        kv_rope=f, kv_scale=f, stream=0), **kw}))
+    assert q8(D_latent=128)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert q8(D_latent=64)[0] == _lib.MLA_ERR_UNSUPPORTED  # 64 latent goes with 16 rope
+    assert q8(T=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert q8(N_kv=1 << 31)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert q8(kv_scale=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert q8(local_latent=_P(FAKE + 8))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert q8(T=0)[0] == 0
 
 
 def test_partition_validation_errors():
@@ -152,6 +164,7 @@ def test_partition_validation_errors():
     assert p(n_vrows=1)[0] == _lib.MLA_ERR_INVALID_ARG  # fewer than 1 per request
     assert p(merge_src=None)[0] == _lib.MLA_ERR_INVALID_ARG
     assert p(T_glob=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert p(block_table=f, bt_stride=0)[0] == _lib.MLA_ERR_INVALID_ARG
 
 
 class _Len(_P):

@@ -1,0 +1,327 @@
+"""GPU parity of the paged latent-KV cache (block table of 64-row blocks) and of fp8
+quantise-on-insert, against the oracle.
+
+Slots, copied rows, fp8 codes and block scales are compared bit for bit; attention values
+meet the same bounds as the packed path (max|O-O_ref| <= 1e-2, 3e-2 for fp8 latent;
+max|LSE-LSE_ref| <= 1e-3). A paged dense run is also bit-identical to the packed run of
+the same workload: paging changes addresses only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import helpers as hp
+from context_mla_prefill_amd import _lib, synth
+from context_mla_prefill_amd import pipeline as pp
+from oracle import kvcache as ok
+from oracle import numerics as on
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL, SPARSE_O_TOL = 1e-2, 1e-3, 3e-2
+NAN_BF16 = 0x7FC0
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def make_block_table(w, seed, spare=5, pad=2):
+    """Each request's ceil(kv_len / 64) blocks drawn without replacement from a pool with
+    spare blocks, in random order; pad columns hold -1 and are never read."""
+    rng = np.random.default_rng(seed)
+    nb = (w.kv_lens.astype(np.int64) + 63) // 64
+    n_blocks = int(nb.sum()) + spare
+    perm = rng.permutation(n_blocks)
+    bt = np.full((w.n_req, int(nb.max(initial=0)) + pad), -1, np.int32)
+    k = 0
+    for b in range(w.n_req):
+        bt[b, :nb[b]] = perm[k:k + nb[b]]
+        k += int(nb[b])
+    return bt, n_blocks
+
+
+def rank_order(plan):
+    """Global tokens in rank-concatenated row order."""
+    return np.concatenate([rp.local_gidx for rp in plan.ranks]).astype(np.int64)
+
+
+def context_rows(w):
+    """(request, position) of every key written before this step (kv_len > q_len)."""
+    reqs, poss = [], []
+    for b in range(w.n_req):
+        ctx = int(w.kv_lens[b] - w.q_lens[b])
+        reqs.append(np.full(ctx, b, np.int64))
+        poss.append(np.arange(ctx, dtype=np.int64))
+    return np.concatenate(reqs), np.concatenate(poss)
+
+
+def check_paged_plan(pl, plan, bt):
+    """Integer outputs bit-exact; slots are the oracle's positions through the block table."""
+    torch.cuda.synchronize()
+    pos, req = hp.token_maps(plan)
+    assert pl.T_glob == plan.T_glob
+    assert np.array_equal(pl.merge_src.cpu().numpy(), plan.merge_src)
+    for r, rp in enumerate(plan.ranks):
+        rows = pl.rank_rows(r)
+        g = rp.local_gidx.astype(np.int64)
+        assert np.array_equal(pl.local_gidx[rows].cpu().numpy(), rp.local_gidx)
+        assert np.array_equal(pl.positions[rows].cpu().numpy(), rp.positions)
+        assert np.array_equal(pl.cu_q[r].cpu().numpy(), rp.cu_seqlens_q)
+        assert np.array_equal(pl.vrow_req[r].cpu().numpy(), rp.vrow_req)
+        assert np.array_equal(pl.vrow_kv_start[r].cpu().numpy(), rp.vrow_kv_start)
+        assert np.array_equal(pl.vrow_kv_len[r].cpu().numpy(), rp.vrow_kv_len)
+        want = ok.paged_rows(bt, req[g], pos[g])
+        assert np.array_equal(pl.slot[rows].cpu().numpy(), want)
+
+
+class DenseCacheRun:
+    """partition -> bf16 insert -> P dense partials -> merge, on a packed or a paged cache."""
+
+    def __init__(self, w, seed=0, paged=True, kv_splits=1):
+        self.w, self.paged, self.kv_splits = w, paged, kv_splits
+        self.plan = plan = hp.oracle_plan(w)
+        print(f"[run] dense {'paged' if paged else 'packed'} {w.name} T={w.T_glob} kv_splits={kv_splits}",
+              flush=True)
+        self.q_bits, self.lat_bits, self.rope_bits = synth.q_rows(w), synth.latent_rows(w), synth.rope_rows(w)
+        self.sink = synth.sink(w)
+        q, lat_full, rope_full = dev_bf16(self.q_bits), dev_bf16(self.lat_bits), dev_bf16(self.rope_bits)
+        if paged:
+            self.bt, n_blocks = make_block_table(w, seed)
+            N = n_blocks * 64
+        else:
+            self.bt, N = None, w.N_kv
+        self.pl = pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P, block_table=self.bt)
+        pp.run_partition(pl)
+        pos, req = hp.token_maps(plan)
+        self.kv_lat = torch.full((N, w.Dl), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        self.kv_rope = torch.full((N, w.Dr), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        # keys written by earlier steps, placed where the cache layout puts them
+        cr, cp = context_rows(w)
+        self.key_rows = lambda b, p: ok.paged_rows(self.bt, b, p) if paged else w.kv_start[b] + p
+        if len(cr):
+            dst = torch.from_numpy(self.key_rows(cr, cp)).cuda()
+            src = torch.from_numpy(w.kv_start[cr] + cp).cuda()
+            self.kv_lat[dst] = lat_full[src]
+            self.kv_rope[dst] = rope_full[src]
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
+        self.sink_d = torch.from_numpy(self.sink).cuda()
+        ranks = []
+        for r, rp in enumerate(plan.ranks):
+            g = torch.from_numpy(rp.local_gidx.astype(np.int64)).cuda()
+            src = torch.from_numpy((w.kv_start[req] + pos)[rp.local_gidx.astype(np.int64)]).cuda()
+            ranks.append(pp.RankInputs(q=q.index_select(0, g).contiguous(), topk=None,
+                                       latent=lat_full.index_select(0, src).contiguous(),
+                                       rope=rope_full.index_select(0, src).contiguous()))
+        for r, ri in enumerate(ranks):
+            _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
+                               _lib.MLA_KV_BF16, N, self.kv_lat, self.kv_rope)
+        for r, ri in enumerate(ranks):
+            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                   kv_splits=kv_splits)
+            _lib.mla_prefill_partial(args)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
+        torch.cuda.synchronize()
+
+    def check_cache(self):
+        """Every key of every request sits bit-exact at its row."""
+        w = self.w
+        reqs = np.concatenate([np.full(int(k), b, np.int64) for b, k in enumerate(w.kv_lens)])
+        poss = np.concatenate([np.arange(int(k), dtype=np.int64) for k in w.kv_lens])
+        rows = self.key_rows(reqs, poss)
+        got_l = host_bits(self.kv_lat)[rows]
+        got_r = host_bits(self.kv_rope)[rows]
+        assert np.array_equal(got_l, self.lat_bits[w.kv_start[reqs] + poss])
+        assert np.array_equal(got_r, self.rope_bits[w.kv_start[reqs] + poss])
+
+    def check_values(self):
+        w, plan = self.w, self.plan
+        toks = np.arange(w.T_glob)
+        ref = hp.oracle_dense(w, plan, self.q_bits, self.lat_bits, self.rope_bits, self.sink, toks)
+        if self.kv_splits == 1:
+            o_cat = on.bf16_to_f64(host_bits(self.bufs.o_cat))
+            lse_cat = self.bufs.lse_cat.cpu().numpy()
+            for r, rp in enumerate(plan.ranks):
+                cat = plan.row_off[r] + np.arange(rp.T_loc)
+                gi = rp.local_gidx.astype(np.int64)
+                hp.compare(f"paged dense rank {r} partial", o_cat[cat], lse_cat[cat],
+                           np.stack([ref[g][0] for g in gi]), np.stack([ref[g][1] for g in gi]), O_TOL, LSE_TOL)
+        o = on.bf16_to_f64(host_bits(self.bufs.o))
+        hp.compare("paged dense merged", o, self.bufs.lse.cpu().numpy(), np.stack([ref[g][2] for g in toks]),
+                   np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
+
+
+PAGED_DENSE = {
+    # seed: (q_lens, kv_lens, P, H, Dl, Dr, kv_splits)
+    401: ([700, 1, 130, 64], [700, 3000, 900, 64], 2, 16, 512, 64, 1),  # prefill, long decode, continuations
+    402: ([300, 5, 1], [300, 77, 200], 3, 4, 64, 16, 1),                # small dims, ragged blocks
+    403: ([1500, 1, 200], [1500, 2100, 333], 2, 16, 512, 64, 3),        # paged + split KV
+}
+
+
+@pytest.mark.parametrize("seed", sorted(PAGED_DENSE))
+def test_paged_dense(gpu_lib, seed):
+    """Paged bf16 cache: plan slots through the block table, the cache after the inserts,
+    every token against the oracle, and bit-identical partials to the packed run."""
+    q, kv, P, H, Dl, Dr, S = PAGED_DENSE[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=Dl, Dr=Dr)
+    run = DenseCacheRun(w, seed=seed, paged=True, kv_splits=S)
+    check_paged_plan(run.pl, run.plan, run.bt)
+    run.check_cache()
+    run.check_values()
+    packed = DenseCacheRun(w, paged=False, kv_splits=S)
+    assert torch.equal(run.bufs.o_cat.view(torch.int16), packed.bufs.o_cat.view(torch.int16))
+    assert torch.equal(run.bufs.lse_cat.view(torch.int32), packed.bufs.lse_cat.view(torch.int32))
+
+
+# ------------------------------------------------------------------ fp8 quantise-on-insert
+
+@pytest.mark.parametrize("dims", [(512, 64), (64, 16)])
+def test_fp8_insert_bit_exact(gpu_lib, dims):
+    """Two insert calls on one cache: fresh blocks, a block opened by the first call and
+    continued by the second, rows into a block opened before both (stored scale, values
+    that saturate), an all-zero block, and slots outside the cache. Codes, scales and rope
+    rows match the oracle bit for bit after each call."""
+    Dl, Dr = dims
+    N = 64 * 8
+    nblk = N // 64
+    rng = np.random.default_rng(Dl)
+    print(f"[run] fp8 insert dims {Dl}+{Dr}", flush=True)
+    codes_o = np.full((N, Dl), 0x7F, np.uint8)
+    scales_o = np.full(nblk, np.nan, np.float32)
+    scales_o[2] = np.float32(0.01)  # block 2 was opened earlier
+    rope_o = np.full((N, Dr), NAN_BF16, np.uint16)
+    codes_d = torch.from_numpy(codes_o).cuda()
+    scales_d = torch.from_numpy(scales_o).cuda()
+    rope_d = torch.from_numpy(rope_o.view(np.int16)).cuda().view(torch.bfloat16)
+    calls = [
+        np.concatenate([rng.permutation(64), 64 + np.arange(10), 128 + np.arange(5, 21), [192, 255, -1, N],
+                        320 + np.arange(64)]),
+        np.concatenate([64 + np.arange(10, 64), 256 + rng.permutation(64)]),
+    ]
+    for ci, slot in enumerate(calls):
+        T = len(slot)
+        x = rng.standard_normal((T, Dl)).astype(np.float32) * np.exp(rng.normal(0, 2, (T, 1))).astype(np.float32)
+        x[np.isin(slot, 320 + np.arange(64))] = 0.0  # block 5 all zero
+        if ci == 0:
+            x[np.isin(slot, 128 + np.arange(5, 21))] *= 10  # saturates against the stored 0.01
+        lat_bits = synth.bf16_bits(x)
+        rope_bits = synth.bf16_bits(rng.standard_normal((T, Dr)).astype(np.float32))
+        slot32 = slot.astype(np.int32)
+        _lib.pcp_kv_insert_fp8(dev_bf16(lat_bits), dev_bf16(rope_bits), torch.from_numpy(slot32).cuda(), T, Dl, Dr,
+                               N, codes_d, rope_d, scales_d)
+        torch.cuda.synchronize()
+        codes_o, scales_o = ok.quantize_insert_fp8(codes_o, scales_o, lat_bits, slot)
+        keep = (slot >= 0) & (slot < N)
+        rope_o[slot[keep]] = rope_bits[keep]
+        got_c = codes_d.cpu().numpy()
+        bad = np.argwhere(got_c != codes_o)
+        assert len(bad) == 0, f"call {ci}: {len(bad)} codes differ, first {bad[:4].tolist()}"
+        assert np.array_equal(scales_d.cpu().numpy().view(np.uint32), scales_o.view(np.uint32)), \
+            f"call {ci}: scales {scales_d.cpu().numpy()} vs {scales_o}"
+        assert np.array_equal(host_bits(rope_d), rope_o)
+    assert np.all(codes_o[320:384] == 0) and scales_o[5] == 1.0
+    assert np.any(codes_o[133:149] & 0x7F == 0x7E)  # saturated codes present
+
+
+class PagedSparseRun:
+    """partition (paged) -> fp8 quantise-on-insert of context and new rows -> P sparse
+    partials -> merge. The oracle quantises the same bf16 rows itself."""
+
+    def __init__(self, w, seed, kv_splits=1):
+        self.w, self.kv_splits = w, kv_splits
+        self.plan = plan = hp.oracle_plan(w)
+        print(f"[run] sparse paged {w.name} T={w.T_glob} kv_splits={kv_splits}", flush=True)
+        self.q_bits, self.lat_bits, self.rope_bits = synth.q_rows(w), synth.latent_rows(w), synth.rope_rows(w)
+        self.topk = synth.topk_rows(w)
+        self.sink = synth.sink(w)
+        self.bt, n_blocks = make_block_table(w, seed)
+        N = n_blocks * 64
+        q, lat_full, rope_full = dev_bf16(self.q_bits), dev_bf16(self.lat_bits), dev_bf16(self.rope_bits)
+        topk_d = torch.from_numpy(self.topk).cuda()
+        self.pl = pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P, block_table=self.bt)
+        pp.run_partition(pl)
+        pos, req = hp.token_maps(plan)
+        self.codes_d = torch.full((N, w.Dl), 0x7F, dtype=torch.uint8, device="cuda")
+        self.scales_d = torch.full((n_blocks,), float("nan"), dtype=torch.float32, device="cuda")
+        self.rope_d = torch.full((N, w.Dr), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        self.codes_o = np.full((N, w.Dl), 0x7F, np.uint8)
+        self.scales_o = np.full(n_blocks, np.nan, np.float32)
+        # 1. the context keys, written by one earlier call
+        cr, cp = context_rows(w)
+        if len(cr):
+            src = w.kv_start[cr] + cp
+            slot = ok.paged_rows(self.bt, cr, cp)
+            _lib.pcp_kv_insert_fp8(dev_bf16(self.lat_bits[src]), dev_bf16(self.rope_bits[src]),
+                                   torch.from_numpy(slot.astype(np.int32)).cuda(), len(src), w.Dl, w.Dr, N,
+                                   self.codes_d, self.rope_d, self.scales_d)
+            self.codes_o, self.scales_o = ok.quantize_insert_fp8(self.codes_o, self.scales_o, self.lat_bits[src],
+                                                                 slot)
+        # 2. this step's rows of every rank in one call (the all-gathered latent KV)
+        g = rank_order(plan)
+        src = w.kv_start[req[g]] + pos[g]
+        _lib.pcp_kv_insert_fp8(lat_full[torch.from_numpy(src).cuda()].contiguous(),
+                               rope_full[torch.from_numpy(src).cuda()].contiguous(), pl.slot, pl.T_total, w.Dl,
+                               w.Dr, N, self.codes_d, self.rope_d, self.scales_d)
+        self.codes_o, self.scales_o = ok.quantize_insert_fp8(self.codes_o, self.scales_o, self.lat_bits[src],
+                                                             ok.paged_rows(self.bt, req[g], pos[g]))
+        self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
+        self.sink_d = torch.from_numpy(self.sink).cuda()
+        for r, rp in enumerate(plan.ranks):
+            gi = torch.from_numpy(rp.local_gidx.astype(np.int64)).cuda()
+            ri = pp.RankInputs(q=q.index_select(0, gi).contiguous(), topk=topk_d.index_select(0, gi).contiguous(),
+                               latent=None, rope=None)
+            args = pp.partial_args(pl, r, ri, self.codes_d, self.rope_d, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=self.scales_d, topk=w.topk,
+                                   window=w.window, kv_splits=kv_splits)
+            _lib.mla_prefill_partial(args)
+        pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
+        torch.cuda.synchronize()
+
+    def check_cache(self):
+        assert np.array_equal(self.codes_d.cpu().numpy(), self.codes_o)
+        assert np.array_equal(self.scales_d.cpu().numpy().view(np.uint32), self.scales_o.view(np.uint32))
+
+    def check_values(self):
+        w, plan = self.w, self.plan
+        toks = np.arange(w.T_glob)
+        ref = hp.oracle_sparse(w, plan, self.q_bits, self.codes_o, self.scales_o, self.rope_bits, self.topk,
+                               self.sink, toks, rows_of=lambda b, keys: ok.paged_rows(self.bt, b, keys))
+        if self.kv_splits == 1:
+            o_cat = on.bf16_to_f64(host_bits(self.bufs.o_cat))
+            lse_cat = self.bufs.lse_cat.cpu().numpy()
+            for r, rp in enumerate(plan.ranks):
+                cat = plan.row_off[r] + np.arange(rp.T_loc)
+                gi = rp.local_gidx.astype(np.int64)
+                hp.compare(f"paged sparse rank {r} partial", o_cat[cat], lse_cat[cat],
+                           np.stack([ref[g][0] for g in gi]), np.stack([ref[g][1] for g in gi]), SPARSE_O_TOL,
+                           LSE_TOL)
+        o = on.bf16_to_f64(host_bits(self.bufs.o))
+        hp.compare("paged sparse merged", o, self.bufs.lse.cpu().numpy(), np.stack([ref[g][2] for g in toks]),
+                   np.stack([ref[g][3] for g in toks]), SPARSE_O_TOL, LSE_TOL)
+
+
+PAGED_SPARSE = {
+    # seed: (q_lens, kv_lens, P, topk, window, kv_splits)
+    # fresh prefill; a decode row over 640 cached keys; a continuation of 512 cached keys;
+    # a continuation whose first new rows land in a block the cached keys opened
+    501: ([700, 1, 300, 200], [700, 641, 812, 300], 2, 128, 64, 1),
+    502: ([900, 1], [1000, 1300], 2, 192, 32, 3),  # paged + split KV, unaligned continuation
+}
+
+
+@pytest.mark.parametrize("seed", sorted(PAGED_SPARSE))
+def test_paged_sparse_quantize_on_insert(gpu_lib, seed):
+    """fp8 sparse path on a paged cache that the library quantised itself: codes and block
+    scales bit-exact against the oracle's quantiser, slots through the block table, and every
+    token's partials and merged output against the oracle on the oracle's own codes."""
+    q, kv, P, topk, window, S = PAGED_SPARSE[seed]
+    w = synth.custom(seed, q, kv, P=P, H=64, Dl=512, Dr=64, topk=topk, window=window, latent_std=1.0)
+    run = PagedSparseRun(w, seed, kv_splits=S)
+    check_paged_plan(run.pl, run.plan, run.bt)
+    run.check_cache()
+    run.check_values()

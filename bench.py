@@ -11,10 +11,15 @@ Prints ONE JSON line. ``value`` is the attention TFLOP/s of the whole step
 HBM). ``roofline`` covers the dominant kernel (the partial attention), with its
 average launch time from HIP events on the launch stream. ``cpu_baseline`` times the
 fp64 oracle on a bounded sample of query rows of the same workload.
+
+``--paged`` keeps the KV in a paged cache of 64-row blocks behind a seeded random block
+table; with the fp8 top-k workload (``--workload 4``) the step then inserts the new rows
+as bf16 and quantises them on insert, in one call for the all-gathered rows of every rank.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -136,6 +141,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=1,
                     help="cut every row's keys into this many ranges (split-KV partials, merged with the ranks)")
+    ap.add_argument("--paged", action="store_true",
+                    help="keep the KV in a paged cache of 64-row blocks (seeded random block table); the fp8 "
+                         "workload then quantises its new bf16 rows on insert, in one call for all ranks")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
                          "(a kernel of known byte count for scaling HBM traffic counters)")
@@ -159,22 +167,65 @@ def main():
 
     t_setup = time.perf_counter()
     q = upload(synth.q_rows(w))
-    if sparse:
+    quantise = sparse and args.paged  # new rows arrive as bf16 and are quantised on insert
+    if sparse and not quantise:
         lat_full = torch.from_numpy(synth.latent_rows(w)).to(dev)
         kv_scale = torch.from_numpy(synth.kv_scales(w)).to(dev)
+    else:
+        # the same N(0, std) draws as the fp8 codes of a sparse workload, kept in bf16
+        lat_full = upload(synth.latent_rows(dataclasses.replace(w, kv_dtype="bf16")))
+        kv_scale = None
+    if sparse:
         topk_host = synth.topk_rows(w)
         topk = torch.from_numpy(topk_host).to(dev)
     else:
-        lat_full = upload(synth.latent_rows(w))
-        kv_scale, topk, topk_host = None, None, None
+        topk, topk_host = None, None
     rope_full = upload(synth.rope_rows(w))
     sink = torch.from_numpy(synth.sink(w)).to(dev)
-    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+    block_table = None
+    if args.paged:
+        rng = np.random.default_rng(2024)
+        nb = (w.kv_lens.astype(np.int64) + 63) // 64
+        perm = rng.permutation(int(nb.sum())).astype(np.int32)
+        block_table = np.zeros((w.n_req, int(nb.max())), np.int32)
+        for b, k0 in enumerate(np.concatenate([[0], np.cumsum(nb)[:-1]])):
+            block_table[b, :nb[b]] = perm[k0:k0 + nb[b]]
+    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P, block_table=block_table)
     pp.run_partition(pl)
     ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk) for r in range(w.P)]
     del q
-    kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
-    kv_rope = rope_full.clone()
+    if args.paged:
+        # every key of every request in its block before the step (context rows stay, the step
+        # re-inserts the new ones)
+        n_cache = int(nb.sum()) * 64
+        bt_d = torch.from_numpy(block_table).to(dev).long()
+        reqs = torch.repeat_interleave(torch.arange(w.n_req, device=dev), torch.from_numpy(w.kv_lens).to(dev).long())
+        starts = torch.from_numpy(np.concatenate([[0], np.cumsum(w.kv_lens.astype(np.int64))[:-1]])).to(dev)
+        pos = torch.arange(w.N_kv, device=dev) - starts[reqs]
+        dst = bt_d[reqs, pos // 64] * 64 + pos % 64
+        src = torch.from_numpy(w.kv_start).to(dev).long()[reqs] + pos
+        kv_rope = torch.empty(n_cache, w.Dr, dtype=torch.bfloat16, device=dev)
+        kv_rope[dst] = rope_full[src]
+        if quantise:
+            kv_lat = torch.empty(n_cache, w.Dl, dtype=torch.uint8, device=dev)
+            kv_scale = torch.empty(n_cache // 64, dtype=torch.float32, device=dev)
+            lat_src = lat_full[src].contiguous()
+            _lib.pcp_kv_insert_fp8(lat_src, kv_rope[dst].contiguous(), dst.int(), w.N_kv, w.Dl, w.Dr, n_cache,
+                                   kv_lat, kv_rope, kv_scale)
+            del lat_src
+        else:
+            kv_lat = torch.empty(n_cache, w.Dl, dtype=torch.bfloat16, device=dev)
+            kv_lat[dst] = lat_full[src]
+        del bt_d, reqs, starts, pos, dst, src
+    else:
+        kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
+        kv_rope = rope_full.clone()
+    n_cache = int(kv_lat.shape[0])
+    if quantise:  # one insert of the all-gathered new rows (rank order)
+        lat_new = torch.cat([ri.latent for ri in ranks])
+        rope_new = torch.cat([ri.rope for ri in ranks])
+        for ri in ranks:
+            ri.latent = ri.rope = None
     S = args.kv_splits
     bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=S)
     kv_dtype = _lib.MLA_KV_FP8_E4M3 if sparse else _lib.MLA_KV_BF16
@@ -184,15 +235,23 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    n_ev = w.P + 1
+    n_ev = w.P + 2
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
               for _ in range(args.steps)]
 
     def step(ev=None):
         pp.run_partition(pl)
-        for r in range(w.P):
-            _lib.pcp_kv_insert(ranks[r].latent, ranks[r].rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
-                               kv_dtype, w.N_kv, kv_lat, kv_rope)
+        if ev:
+            ev[w.P + 1][0].record(stream)
+        if quantise:
+            _lib.pcp_kv_insert_fp8(lat_new, rope_new, pl.slot, pl.T_total, w.Dl, w.Dr, n_cache, kv_lat, kv_rope,
+                                   kv_scale)
+        else:
+            for r in range(w.P):
+                _lib.pcp_kv_insert(ranks[r].latent, ranks[r].rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl,
+                                   w.Dr, kv_dtype, n_cache, kv_lat, kv_rope)
+        if ev:
+            ev[w.P + 1][1].record(stream)
         for r in range(w.P):
             if ev:
                 ev[r][0].record(stream)
@@ -227,10 +286,11 @@ def main():
     t_rank = [float(np.mean([events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)]))
               for r in range(w.P)]
     t_merge = float(np.mean([events[k][w.P][0].elapsed_time(events[k][w.P][1]) for k in range(args.steps)]))
+    t_insert = float(np.mean([events[k][w.P + 1][0].elapsed_time(events[k][w.P + 1][1]) for k in range(args.steps)]))
     avg_launch_ms = float(np.mean(t_rank))
     achieved = (flops_step / w.P) / (avg_launch_ms * 1e-3) / 1e12
     mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl, S)
-    att_traffic, merge_traffic = measured_traffic(args.workload)
+    att_traffic, merge_traffic = measured_traffic(args.workload) if not args.paged else (None, None)
 
     out = {
         "metric": "PCP-shard MLA prefill attention TFLOP/s + MFMA% at 1 GPU; merge GB/s",
@@ -242,7 +302,9 @@ def main():
         "data": "synthetic (seeded N(0,1)*0.5 bf16 q/latent/rope, N(0,1) sink)",
         "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
                    "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU",
-                   **({"kv_splits": S} if S > 1 else {})},
+                   **({"kv_splits": S} if S > 1 else {}),
+                   **({"kv_cache": "paged, 64-row blocks" + (", fp8 quantise-on-insert" if quantise else "")}
+                      if args.paged else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": att_traffic},
         "attention": {"rank_ms": [round(x, 3) for x in t_rank],
@@ -252,6 +314,8 @@ def main():
         "merge": {"ms": round(t_merge, 4), "GB/s": round(mbytes / (t_merge * 1e-3) / 1e9, 1),
                   "frac_hbm": round(mbytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": mbytes,
                   "traffic": merge_traffic},
+        "insert": {"ms": round(t_insert, 4),
+                   "kind": "fp8 quantise-on-insert, one call" if quantise else f"byte copy, {w.P} calls"},
         "setup_s": round(setup_s, 1),
     }
     if sparse:

@@ -1,9 +1,11 @@
 """Device plumbing for one PCP prefill step on one GPU.
 
 Allocates the caller-owned buffers the C ABI expects and issues the calls in order:
-``pcp_partition`` -> ``pcp_kv_insert`` (per rank) -> ``mla_prefill_partial`` (per rank,
-one after another) -> ``pcp_lse_merge``. Tensors are torch device tensors (memory and
-streams only); every step runs in the library's HIP kernels.
+``pcp_partition`` -> ``pcp_kv_insert`` (per rank; or one ``pcp_kv_insert_fp8`` of every
+rank's rows) -> ``mla_prefill_partial`` (per rank, one after another) -> ``pcp_lse_merge``.
+The KV cache is packed per request or paged (a block table of 64-row blocks). Tensors are
+torch device tensors (memory and streams only); every step runs in the library's HIP
+kernels.
 """
 from __future__ import annotations
 
@@ -85,14 +87,26 @@ class RankInputs:
     rope: torch.Tensor  # [T_loc, Dr]
 
 
-def rank_inputs(pl: DevicePlan, r: int, q_glob, latent_full, rope_full, topk_glob=None) -> RankInputs:
+def packed_rows(pl: DevicePlan, r: int) -> torch.Tensor:
+    """Row of each of rank r's local tokens in a packed per-request KV layout
+    (kv_start[request] + position): where its latent/rope source row sits in the inputs.
+    Equal to the plan's slots when the cache itself is packed."""
     rows = pl.rank_rows(r)
     gidx = pl.local_gidx[rows].long()
-    slots = pl.slot[rows].long()
+    req = torch.searchsorted(pl.cu_glob.long(), gidx, right=True) - 1
+    return pl.kv_start.long()[req] + pl.positions[rows].long()
+
+
+def rank_inputs(pl: DevicePlan, r: int, q_glob, latent_full, rope_full, topk_glob=None) -> RankInputs:
+    """Rank r's query rows (and selected keys) and the new KV rows it contributes, gathered
+    from packed global inputs (set-up, not part of the step)."""
+    rows = pl.rank_rows(r)
+    gidx = pl.local_gidx[rows].long()
+    src = packed_rows(pl, r)
     return RankInputs(q=q_glob.index_select(0, gidx).contiguous(),
                       topk=None if topk_glob is None else topk_glob.index_select(0, gidx).contiguous(),
-                      latent=latent_full.index_select(0, slots).contiguous(),
-                      rope=rope_full.index_select(0, slots).contiguous())
+                      latent=latent_full.index_select(0, src).contiguous(),
+                      rope=rope_full.index_select(0, src).contiguous())
 
 
 @dataclass

@@ -20,9 +20,13 @@ What it computes, and where the pages fix it:
 * ``merge``: the log-sum-exp merge of per-rank partial (O, LSE) with the sink
   applied once in the final denominator ("[DeepSeekV4][PCP] Enable context-parallel
   prefill for hybrid KV and MegaMoE", "Purpose" and "Main challenges").
-* ``numerics``: exact bf16 decode, bf16 round-to-nearest-even, OCP E4M3FN decode.
+* ``numerics``: exact bf16 decode, bf16 round-to-nearest-even, OCP E4M3FN decode and
+  nearest-even encode.
+* ``kvcache``: paged addressing of a cache of 64-row blocks and fp8 quantise-on-insert with
+  one fp32 scale per block ("[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch
+  Arguments": fp8 MLA KV cache, block size 64).
 
 Every function is pinned by tests marked ``not gpu`` against brute force, closed
 forms, library special cases and the pages' worked partition pictures.
 """
-from . import numerics, partition, attention, merge  # noqa: F401
+from . import numerics, partition, attention, merge, kvcache  # noqa: F401

@@ -139,6 +139,20 @@ mla_status pcp_kv_insert_fp8(const void* local_latent, const void* local_rope, c
     return MLA_OK;
 }
 
+mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* positions, int32_t T, int32_t k,
+                              int32_t* topk_idx, void* stream) {
+    if (T < 0 || ld < 1 || ld % 4 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "sparse_topk_select: sizes out of range (T=%d, ld=%lld; ld %% 4 == 0)", T,
+                    (long long)ld);
+    if (k < 1 || k > 2048) return fail(MLA_ERR_UNSUPPORTED, "sparse_topk_select: k=%d outside 1..2048", k);
+    if (T == 0) return MLA_OK;
+    if (!scores || !positions || !topk_idx) return fail(MLA_ERR_INVALID_ARG, "sparse_topk_select: null pointer");
+    if (!aligned16(scores)) return fail(MLA_ERR_INVALID_ARG, "sparse_topk_select: scores must be 16-byte aligned");
+    hipError_t e = launch_topk_select(scores, ld, positions, T, k, topk_idx, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "sparse_topk_select: %s", hipGetErrorString(e));
+    return MLA_OK;
+}
+
 // The sparse kernel addresses KV rows through 32-bit buffer offsets: N_kv * 512 < 2^32.
 constexpr int64_t kSparseMaxKv = (int64_t(1) << 23) - 1;
 

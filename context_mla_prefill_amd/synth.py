@@ -20,9 +20,19 @@ Workloads (the five shapes the path is measured and checked on):
    latent KV stored as fp8-e4m3 with one fp32 scale per 64 packed KV rows.
 5. mixed varlen: 8 prefills with lengths log-uniform in [4096, 65536) and 64 decode
    rows (1 token each) with contexts log-uniform in [1024, 32768), 4 ranks, 16 heads.
+6. chunked prefill: one step of 32768 batched tokens, 4 ranks, 16 heads: the last 16384-
+   token chunk of a 131072-token prompt, an 8192-token chunk at context 40960, a fresh
+   8108-token prefill, prefills at the replication threshold (8 new tokens = 2P, split;
+   7 new tokens, and 5 new tokens after 895 cached ones, replicated) and 64 decode rows
+   with contexts log-uniform in [1024, 32768).
 
 q / latent / rope values ~ N(0,1)*0.5 (the fp8 latent of workload 4 ~ N(0,1)),
 sink ~ N(0,1) per head, softmax scale fp32(1/sqrt(latent+rope)).
+
+Index scores (the top-k selection's input) are not drawn from a stream but hashed from
+(workload, global token, key position) with MurmurHash3's 32-bit finaliser, so any row can be
+rebuilt alone, on the host (numpy) or on the device (torch integer ops, bit-identical):
+score = (h >> 8) * 2^-24, uniform on a 2^-24 grid in [0, 1) (ties happen, as with real logits).
 """
 from __future__ import annotations
 
@@ -112,6 +122,14 @@ def _config5_lengths() -> tuple[np.ndarray, np.ndarray]:
     return q.astype(np.int32), kv.astype(np.int32)
 
 
+def _config6_lengths() -> tuple[np.ndarray, np.ndarray]:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([6, T_LENGTHS, 0])))
+    ctx = np.floor(np.exp(rng.uniform(math.log(1024), math.log(32768), 64))).astype(np.int64)
+    q = np.array([16384, 8192, 8108, 8, 7, 5] + [1] * 64, dtype=np.int64)
+    kv = np.concatenate([[131072, 49152, 8108, 4000, 7, 900], ctx])
+    return q.astype(np.int32), kv.astype(np.int32)
+
+
 def workload(cfg: int) -> Workload:
     if cfg == 1:
         return Workload(1, "tiny dense T=256 P=2 H=4 64+16", [256], [256], P=2, H=4, Dl=64, Dr=16)
@@ -125,6 +143,10 @@ def workload(cfg: int) -> Workload:
     if cfg == 5:
         q, kv = _config5_lengths()
         return Workload(5, "mixed varlen 8 prefill + 64 decode P=4 H=16 512+64", q, kv, P=4, H=16, Dl=512, Dr=64)
+    if cfg == 6:
+        q, kv = _config6_lengths()
+        return Workload(6, "chunked prefill step 32768 tokens (continuations + decode) P=4 H=16 512+64", q, kv,
+                        P=4, H=16, Dl=512, Dr=64)
     raise ValueError(f"unknown workload {cfg}")
 
 
@@ -238,6 +260,54 @@ def _fp8_tiles(w: Workload, tile0: int, tile1: int, want_codes: bool = True):
     t = torch.clamp(t, -FP8_MAX, FP8_MAX)
     codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(nt * FP8_TILE, w.Dl)
     return codes[:n], scale
+
+
+# --------------------------------------------------------------------------- index scores
+
+_M32 = 0xFFFFFFFF
+
+
+def _fmix32(x):
+    """MurmurHash3's 32-bit finaliser on uint32 numpy values (or int64 torch tensors holding
+    32-bit values); wraps modulo 2^32."""
+    x = x ^ (x >> 16)
+    x = (x * 0x85EBCA6B) & _M32
+    x = x ^ (x >> 13)
+    x = (x * 0xC2B2AE35) & _M32
+    return x ^ (x >> 16)
+
+
+def _score_keys(cfg: int):
+    return _fmix32(np.uint64((cfg * 0x9E3779B9 + 0x632BE5AB) & _M32))
+
+
+def index_scores(w: Workload, tokens, n_cols: int) -> np.ndarray:
+    """fp32 [len(tokens), n_cols]: index scores of the given global tokens against key
+    positions 0..n_cols-1 (hash of workload, token, position; see the module header)."""
+    tok = np.asarray(tokens, dtype=np.uint64)
+    rk = _fmix32((tok ^ _score_keys(w.cfg)) & np.uint64(_M32))
+    ck = _fmix32((np.arange(n_cols, dtype=np.uint64) * np.uint64(0x27D4EB2F)) & np.uint64(_M32))
+    h = _fmix32(rk[:, None] ^ ck[None, :])
+    return ((h >> np.uint64(8)).astype(np.float32) * np.float32(2.0 ** -24)).astype(np.float32)
+
+
+def index_scores_device(w: Workload, tokens, n_cols: int, out=None, rows_per_chunk: int = 256):
+    """The same scores as :func:`index_scores`, built on the tokens' device with torch integer
+    ops (chunks of rows); ``tokens`` is an int tensor, ``out`` an fp32 [len(tokens), >= n_cols]
+    tensor (allocated when None)."""
+    import torch
+
+    dev = tokens.device
+    T = int(tokens.shape[0])
+    if out is None:
+        out = torch.empty(T, n_cols, dtype=torch.float32, device=dev)
+    ck = _fmix32((torch.arange(n_cols, dtype=torch.int64, device=dev) * 0x27D4EB2F) & _M32)
+    key = int(_score_keys(w.cfg))
+    for a in range(0, T, rows_per_chunk):
+        rk = _fmix32((tokens[a:a + rows_per_chunk].to(torch.int64) ^ key) & _M32)
+        h = _fmix32(rk[:, None] ^ ck[None, :])
+        out[a:a + rows_per_chunk, :n_cols] = (h >> 8).to(torch.float32) * (2.0 ** -24)
+    return out
 
 
 def sink(w: Workload) -> np.ndarray:

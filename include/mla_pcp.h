@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define MLA_PCP_ABI_VERSION 3
+#define MLA_PCP_ABI_VERSION 4
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -156,6 +156,27 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
 mla_status pcp_kv_insert_fp8(const void* local_latent, const void* local_rope, const int32_t* slot,
                              int32_t T, int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent,
                              void* kv_rope, float* kv_scale, void* stream);
+
+/*
+ * sparse_topk_select — per query row, the k key positions of its causal prefix with the
+ * largest index scores: the selected-index input of the sparse partial (the indexer's top-k
+ * ahead of sparse MLA, "DeepSeek-V4.1: Prefill support CP with multistream forward prepare
+ * (4/N)", "Modifications" and its commit list, "Indexer ... uses topk_v2"). The scores'
+ * producer, the indexer, needs trained weights and is not part of this library.
+ * Row i has n = min(positions[i] + 1, ld) keys with scores scores[i][0..n):
+ *   n <= k: topk_idx[i] = 0, 1, ..., n-1, then -1 pads;
+ *   n > k:  the k indices j in [0, n) with the largest scores, equal scores taken by the
+ *           smaller index (-0 equals +0), written in increasing order.
+ *  scores     device fp32 [T][ld], 16-byte aligned, ld % 4 == 0. NaN is not a score (a row
+ *             holding one still gets k distinct in-range indices).
+ *  positions  device int32 [T], e.g. the partition's positions of one rank's rows.
+ *  topk_idx   device int32 [T][k] (written); with k = mla_partial_args.topk it is that
+ *             call's topk_idx.
+ * Errors: INVALID_ARG (null, T < 0, ld < 1, ld % 4 != 0, misaligned scores); UNSUPPORTED
+ * (k outside 1..2048); HIP.
+ */
+mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* positions, int32_t T, int32_t k,
+                              int32_t* topk_idx, void* stream);
 
 /*
  * mla_prefill_partial — one rank's partial MLA attention against the full KV, without

@@ -153,6 +153,21 @@ def test_merge_and_insert_validation_errors():
     assert q8(T=0)[0] == 0
 
 
+def test_topk_select_validation_errors():
+    f = _P(FAKE)
+    sel = lambda **kw: _status(lambda: _lib.sparse_topk_select(**{**dict(
+        scores=f, ld=4096, positions=f, T=8, k=2048, topk_idx=f, stream=0), **kw}))
+    assert sel(k=0)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert sel(k=2049)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert sel(ld=4094)[0] == _lib.MLA_ERR_INVALID_ARG  # rows not 16-byte aligned
+    assert sel(ld=0)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert sel(T=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert sel(scores=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert sel(topk_idx=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert sel(scores=_P(FAKE + 4))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert sel(T=0)[0] == 0
+
+
 def test_partition_validation_errors():
     f = _P(FAKE)
     p = lambda **kw: _status(lambda: _lib.pcp_partition(**{**dict(

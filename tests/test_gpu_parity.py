@@ -279,6 +279,18 @@ def test_mixed_varlen_decode_sampled(gpu_lib):
     _sampled_run(5, n_random=128)
 
 
+def test_chunked_prefill_sampled(gpu_lib):
+    """One chunked-prefill step of 32768 tokens, P=4: continuation chunks over 114688 and
+    40960 cached keys, a fresh prefill, prefills at the replication threshold (8 = 2P new
+    tokens split, 7 and 5 replicated) and 64 decode rows. Plan and insert in full; the ends
+    of every virtual row and random tokens against the oracle."""
+    run = _sampled_run(6, n_random=128)
+    # the threshold: a request with q_len >= 2P is split into 2P chunks, a shorter one replicated
+    for b, split in ((3, True), (4, False), (5, False)):
+        n = sum(int(np.sum(rp.vrow_req == b)) for rp in run.plan.ranks)
+        assert n == (2 * run.w.P if split else run.w.P), (b, n)
+
+
 # ----------------------------------------------------------------------------- sparse fp8
 
 SPARSE_O_TOL = 3e-2

@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--paged", action="store_true",
                     help="keep the KV in a paged cache of 64-row blocks (seeded random block table); the fp8 "
                          "workload then quantises its new bf16 rows on insert, in one call for all ranks")
+    ap.add_argument("--select", action="store_true",
+                    help="top-k workload: the step also selects every rank's top-k indices on the GPU from "
+                         "hashed index scores (sparse_topk_select), instead of taking them as an input")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
                          "(a kernel of known byte count for scaling HBM traffic counters)")
@@ -175,7 +178,11 @@ def main():
         # the same N(0, std) draws as the fp8 codes of a sparse workload, kept in bf16
         lat_full = upload(synth.latent_rows(dataclasses.replace(w, kv_dtype="bf16")))
         kv_scale = None
-    if sparse:
+    select = sparse and args.select
+    if select:  # filled by the selection inside the step
+        topk_host = None
+        topk = torch.full((w.T_glob, w.topk), -1, dtype=torch.int32, device=dev)
+    elif sparse:
         topk_host = synth.topk_rows(w)
         topk = torch.from_numpy(topk_host).to(dev)
     else:
@@ -194,6 +201,9 @@ def main():
     pp.run_partition(pl)
     ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk) for r in range(w.P)]
     del q
+    if select:  # per rank: fp32 index scores [T_loc][ld] of its rows, built on the device
+        ld_s = (int(w.kv_lens.max()) + 3) // 4 * 4
+        scores_r = [synth.index_scores_device(w, pl.local_gidx[pl.rank_rows(r)].long(), ld_s) for r in range(w.P)]
     if args.paged:
         # every key of every request in its block before the step (context rows stay, the step
         # re-inserts the new ones)
@@ -235,12 +245,20 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    n_ev = w.P + 2
+    n_ev = w.P + 3
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
               for _ in range(args.steps)]
 
     def step(ev=None):
         pp.run_partition(pl)
+        if select:
+            if ev:
+                ev[w.P + 2][0].record(stream)
+            for r in range(w.P):
+                _lib.sparse_topk_select(scores_r[r], ld_s, pl.positions[pl.rank_rows(r)], pl.T_loc[r], w.topk,
+                                        ranks[r].topk)
+            if ev:
+                ev[w.P + 2][1].record(stream)
         if ev:
             ev[w.P + 1][0].record(stream)
         if quantise:
@@ -277,6 +295,10 @@ def main():
     # algorithmic work from the device plan's own positions
     pos_r = [pl.positions[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
     if sparse:
+        if select:  # the selected sets of the last step, gathered back to global token order
+            topk_host = np.empty((w.T_glob, w.topk), np.int32)
+            for r in range(w.P):
+                topk_host[pl.local_gidx[pl.rank_rows(r)].cpu().numpy()] = ranks[r].topk.cpu().numpy()
         n_keys = sparse_set_sizes(topk_host, w)
         gidx_r = [pl.local_gidx[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
         flops_r = [float(2 * (w.Dl + w.Dr + w.Dl) * w.H) * float(n_keys[g].sum()) for g in gidx_r]
@@ -325,6 +347,14 @@ def main():
         gbs = float(np.mean([b / (t * 1e-3) / 1e9 for b, t in zip(gbytes_r, t_rank)]))
         out["gather"] = {"bytes_per_rank": [round(b) for b in gbytes_r], "GB/s": round(gbs, 1),
                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    if select:
+        t_sel = float(np.mean([events[k][w.P + 2][0].elapsed_time(events[k][w.P + 2][1]) for k in range(args.steps)]))
+        n_scores = float(sum((pos_r[r].astype(np.int64) + 1).sum() for r in range(w.P)))
+        sel_bytes = n_scores * 4 + w.T_glob * w.topk * 4  # every prefix score read once, indices written
+        out["topk_select"] = {"ms": round(t_sel, 3), "GB/s": round(sel_bytes / (t_sel * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(sel_bytes / (t_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "bytes": sel_bytes}
+        out["config"]["topk_source"] = "selected on the GPU from hashed index scores"
     if args.calib_copy:
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)

@@ -12,12 +12,15 @@
 //      the sample rank chosen so that about (k + CAND) / 2 scores of a row lie at or above it;
 //   2. one pass gathers every score >= t0 (key and index) into LDS, at most CAND of them;
 //   3. an exact radix select (four 8-bit digits, LDS histograms) over the gathered keys gives
-//      the k-th largest key thr and how many keys equal to thr are taken;
-//   4. one ordered pass writes the indices of keys > thr, and of the first `need` keys == thr,
-//      at their rank among the selected ones (a workgroup prefix sum per 2048 scores).
-// When fewer than k or more than CAND scores reach t0 (rows far from i.i.d., e.g. sorted or
-// heavily tied), step 3 runs over the row in memory instead (four passes). Rows of at most
-// CAND scores are loaded into LDS whole and never re-read.
+//      the k-th largest key thr and how many keys equal to thr are taken; when more keys equal
+//      thr than are taken, a second select over their indices finds the cut;
+//   4. the k selected indices are marked in an LDS bitmap over the row and written in order
+//      (a workgroup prefix sum of the words' popcounts).
+// So the row is read once. When fewer than k or more than CAND scores reach t0 (rows far from
+// i.i.d., e.g. sorted or heavily tied), step 3 runs over the row in memory instead (four
+// passes) and an ordered pass over the row writes the indices of keys > thr and of the first
+// `need` keys == thr at their rank (a workgroup prefix sum per 2048 scores). Rows of at most
+// CAND scores are loaded into LDS whole and take the ordered pass from LDS.
 #include "internal.h"
 
 namespace mla {
@@ -26,6 +29,8 @@ namespace {
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int NW = NT / 64;
 constexpr int CAND = 6144;     // LDS candidates (4-byte key + 4-byte index each)
+constexpr int PER_THREAD = CAND / NT;
+constexpr int UNROLL = 8;      // float4 loads per thread and gather step (two steps in flight)
 constexpr int NSAMP = 2048;    // sampled scores for the threshold estimate
 constexpr int TILE = NT * 4;   // scores per ordered-pass step (4 consecutive per thread)
 
@@ -42,8 +47,9 @@ struct Shared {
     int32_t idx[CAND];
     uint32_t hist[256];
     uint32_t wsum[NW];
-    uint32_t sel[2];
+    uint32_t sel[3];
     uint32_t count;
+    uint32_t orbits;
 };
 
 // Exclusive prefix sum of v over the workgroup; `total` gets the sum. Two barriers.
@@ -71,12 +77,38 @@ __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, Shared& sh, ui
 
 // The rank-th largest key (1-based) among count keys produced by key_at(i), by four 8-bit
 // radix digits from the top. On return `rank` holds how many keys equal to the result are
-// among the rank largest. Every thread returns the same values.
-template <class KeyAt>
-__device__ uint32_t select_rank(KeyAt key_at, int64_t count, uint32_t& rank, Shared& sh) {
+// among the rank largest and `equal` how many keys equal it. Every thread returns the same
+// values.
+// With SKIP (keys in LDS) the digits above the highest bit in which two keys differ are
+// taken from the first key without a histogram: that spares passes in which every key would
+// fall in one bin and every atomic would hit one address.
+template <bool SKIP, class KeyAt>
+__device__ uint32_t select_rank(KeyAt key_at, int64_t count, uint32_t& rank, uint32_t& equal, Shared& sh) {
     const int tid = threadIdx.x;
     uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    int top_shift = 24;
+    if constexpr (SKIP) {
+        const uint32_t k0 = key_at(0);
+        uint32_t x = 0;
+        for (int64_t i = tid; i < count; i += NT) x |= key_at(i) ^ k0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o, 64);
+        if (tid == 0) sh.orbits = 0;
+        __syncthreads();
+        if ((tid & 63) == 0 && x) atomicOr(&sh.orbits, x);
+        __syncthreads();
+        x = sh.orbits;
+        if (x == 0) {  // every key equals k0
+            equal = (uint32_t)count;
+            return k0;
+        }
+        top_shift = ((31 - __builtin_clz(x)) >> 3) << 3;
+        if (top_shift < 24) {
+            mask = ~((1u << (top_shift + 8)) - 1u);
+            prefix = k0 & mask;
+        }
+    }
+    for (int shift = top_shift; shift >= 0; shift -= 8) {
         for (int b = tid; b < 256; b += NT) sh.hist[b] = 0;
         __syncthreads();
         for (int64_t i = tid; i < count; i += NT) {
@@ -105,6 +137,7 @@ __device__ uint32_t select_rank(KeyAt key_at, int64_t count, uint32_t& rank, Sha
                     if (rank <= above + c[e]) {
                         sh.sel[0] = 255u - 4u * tid - e;
                         sh.sel[1] = rank - above;
+                        sh.sel[2] = c[e];
                         break;
                     }
                     above += c[e];
@@ -115,6 +148,7 @@ __device__ uint32_t select_rank(KeyAt key_at, int64_t count, uint32_t& rank, Sha
         prefix |= sh.sel[0] << shift;
         mask |= 255u << shift;
         rank = sh.sel[1];
+        equal = sh.sel[2];
     }
     return prefix;
 }
@@ -135,13 +169,13 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
         return;
     }
 
-    uint32_t thr, need;
+    uint32_t thr, need, equal;
     const bool whole = n <= CAND;
     if (whole) {
         for (int64_t i = tid; i < n; i += NT) sh.key[i] = order_key(srow[i]);
         __syncthreads();
         need = (uint32_t)k;
-        thr = select_rank([&](int64_t i) { return sh.key[i]; }, n, need, sh);
+        thr = select_rank<true>([&](int64_t i) { return sh.key[i]; }, n, need, equal, sh);
     } else {
         // 1. threshold estimate: sample block b starts at floor(b * n / 32) rounded down to 4
         for (int i = tid; i < NSAMP; i += NT) {
@@ -151,42 +185,103 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
         if (tid == 0) sh.count = 0;
         __syncthreads();
         uint32_t j = (uint32_t)min((int64_t)NSAMP, max((int64_t)1, (int64_t)(k + CAND) / 2 * NSAMP / n));
-        const uint32_t t0 = select_rank([&](int64_t i) { return sh.key[i]; }, NSAMP, j, sh);
-        // 2. gather keys >= t0 (slots by a wave-aggregated counter)
-        for (int64_t base = (int64_t)tid * 4; base < n; base += TILE) {
-            float4 v;
-            if (base + 4 <= n) {
-                v = *reinterpret_cast<const float4*>(srow + base);
-            } else {
-                v.x = srow[base];
-                v.y = base + 1 < n ? srow[base + 1] : -INFINITY;
-                v.z = base + 2 < n ? srow[base + 2] : -INFINITY;
-                v.w = -INFINITY;
-            }
-            const float e4[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t t0 = select_rank<true>([&](int64_t i) { return sh.key[i]; }, NSAMP, j, equal, sh);
+        // 2. gather keys >= t0 (slots by a wave-aggregated counter); the loads of the next step
+        //    are issued before the current one is processed
+        auto load_step = [&](float4 (&v)[UNROLL], int64_t b0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t key = order_key(e4[e]);
-                const bool take = base + e < n && key >= t0;
-                const uint64_t bal = __ballot(take);
-                if (bal == 0) continue;  // wave-uniform
-                uint32_t slot0 = 0;
-                if (lane == 0) slot0 = atomicAdd(&sh.count, (uint32_t)__popcll(bal));
-                slot0 = __shfl(slot0, 0, 64);
-                const uint32_t slot = slot0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1));
-                if (take && slot < CAND) {
-                    sh.key[slot] = key;
-                    sh.idx[slot] = (int32_t)(base + e);
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t base = b0 + u * TILE;
+                if (base + 4 <= n) {
+                    v[u] = *reinterpret_cast<const float4*>(srow + base);
+                } else {
+                    v[u].x = base < n ? srow[base] : -INFINITY;
+                    v[u].y = base + 1 < n ? srow[base + 1] : -INFINITY;
+                    v[u].z = base + 2 < n ? srow[base + 2] : -INFINITY;
+                    v[u].w = -INFINITY;
                 }
             }
+        };
+        float4 v[UNROLL], vn[UNROLL];
+        if ((int64_t)tid * 4 < n) load_step(v, (int64_t)tid * 4);
+        for (int64_t b0 = (int64_t)tid * 4; b0 < n; b0 += UNROLL * TILE) {
+            if (b0 + UNROLL * TILE < n) load_step(vn, b0 + UNROLL * TILE);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t base = b0 + u * TILE;
+                const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t key = order_key(e4[e]);
+                    const bool take = base + e < n && key >= t0;
+                    const uint64_t bal = __ballot(take);
+                    if (bal == 0) continue;  // wave-uniform
+                    uint32_t slot0 = 0;
+                    if (lane == 0) slot0 = atomicAdd(&sh.count, (uint32_t)__popcll(bal));
+                    slot0 = __shfl(slot0, 0, 64);
+                    const uint32_t slot = slot0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1));
+                    if (take && slot < CAND) {
+                        sh.key[slot] = key;
+                        sh.idx[slot] = (int32_t)(base + e);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[u] = vn[u];
         }
         __syncthreads();
         const uint32_t c = sh.count;
         need = (uint32_t)k;
         if (c >= (uint32_t)k && c <= (uint32_t)CAND) {
-            thr = select_rank([&](int64_t i) { return sh.key[i]; }, c, need, sh);
+            // 3. every selected key is a candidate (t0 <= thr): select among them in LDS
+            thr = select_rank<true>([&](int64_t i) { return sh.key[i]; }, c, need, equal, sh);
+            const int nwords = (int)((n + 31) >> 5);
+            if (nwords <= CAND) {  // else the ordered pass below
+                int32_t cut = INT32_MAX;  // keys == thr are taken up to this index
+                if (equal > need) {
+                    uint32_t r = need, e2;
+                    cut = (int32_t)~select_rank<true>(
+                        [&](int64_t i) { return sh.key[i] == thr ? ~(uint32_t)sh.idx[i] : 0u; }, c, r, e2, sh);
+                }
+                // 4. mark the k selected indices in a bitmap over the row (it overwrites the keys,
+                //    so every thread first takes its candidates' verdicts into registers)
+                int32_t mine[PER_THREAD];
+#pragma unroll
+                for (int q = 0; q < PER_THREAD; ++q) {
+                    const uint32_t i = (uint32_t)(tid + q * NT);
+                    mine[q] = -1;
+                    if (i < c && (sh.key[i] > thr || (sh.key[i] == thr && sh.idx[i] <= cut))) mine[q] = sh.idx[i];
+                }
+                __syncthreads();
+                uint32_t* bits = sh.key;
+                for (int i = tid; i < nwords; i += NT) bits[i] = 0;
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < PER_THREAD; ++q)
+                    if (mine[q] >= 0) atomicOr(&bits[mine[q] >> 5], 1u << (mine[q] & 31));
+                __syncthreads();
+                // thread t owns words [t * W, t * W + W): their set bits, in order, after the
+                // set bits of all lower words
+                const int W = (nwords + NT - 1) / NT;
+                uint32_t cnt = 0;
+                for (int q = 0; q < W; ++q) {
+                    const int wi = tid * W + q;
+                    cnt += wi < nwords ? (uint32_t)__popc(bits[wi]) : 0u;
+                }
+                uint32_t total;
+                uint32_t pos = wg_exclusive_scan(cnt, sh, total);
+                for (int q = 0; q < W; ++q) {
+                    const int wi = tid * W + q;
+                    uint32_t b = wi < nwords ? bits[wi] : 0u;
+                    while (b) {
+                        orow[pos++] = wi * 32 + (__builtin_ffs((int)b) - 1);
+                        b &= b - 1;
+                    }
+                }
+                return;
+            }
         } else {
-            thr = select_rank([&](int64_t i) { return order_key(srow[i]); }, n, need, sh);
+            thr = select_rank<false>([&](int64_t i) { return order_key(srow[i]); }, n, need, equal, sh);
         }
     }
 

@@ -147,6 +147,9 @@ def main():
     ap.add_argument("--select", action="store_true",
                     help="top-k workload: the step also selects every rank's top-k indices on the GPU from "
                          "hashed index scores (sparse_topk_select), instead of taking them as an input")
+    ap.add_argument("--in-kernel-dequant", action="store_true",
+                    help="top-k workload: the sparse kernel dequantises the fp8 rows of every tile itself, instead "
+                         "of reading a bf16 workspace that pcp_kv_dequant_fp8 fills once per step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
                          "(a kernel of known byte count for scaling HBM traffic counters)")
@@ -239,13 +242,20 @@ def main():
     S = args.kv_splits
     bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=S)
     kv_dtype = _lib.MLA_KV_FP8_E4M3 if sparse else _lib.MLA_KV_BF16
-    args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, kv_dtype=kv_dtype,
-                              kv_scale=kv_scale, topk=w.topk, window=w.window, kv_splits=S) for r in range(w.P)]
+    use_ws = sparse and not args.in_kernel_dequant
+    if use_ws:  # the fp8 cache's blocks dequantised once per step into a bf16 workspace
+        ws = torch.empty(n_cache, w.Dl, dtype=torch.bfloat16, device=dev)
+        ws_blocks = torch.arange((n_cache + 63) // 64, dtype=torch.int32, device=dev)
+        args_r = [pp.partial_args(pl, r, ranks[r], ws, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, topk=w.topk,
+                                  window=w.window, kv_splits=S) for r in range(w.P)]
+    else:
+        args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, kv_dtype=kv_dtype,
+                                  kv_scale=kv_scale, topk=w.topk, window=w.window, kv_splits=S) for r in range(w.P)]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     stream = torch.cuda.current_stream()
-    n_ev = w.P + 3
+    n_ev = w.P + 4
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
               for _ in range(args.steps)]
 
@@ -270,6 +280,12 @@ def main():
                                    w.Dr, kv_dtype, n_cache, kv_lat, kv_rope)
         if ev:
             ev[w.P + 1][1].record(stream)
+        if use_ws:
+            if ev:
+                ev[w.P + 3][0].record(stream)
+            _lib.pcp_kv_dequant_fp8(kv_lat, kv_scale, n_cache, w.Dl, ws_blocks, int(ws_blocks.numel()), ws)
+            if ev:
+                ev[w.P + 3][1].record(stream)
         for r in range(w.P):
             if ev:
                 ev[r][0].record(stream)
@@ -341,12 +357,21 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if sparse:
-        # algorithmic gather: every key of a query's set once per 64-head workgroup, fp8
-        # latent row + bf16 rope row + its fp32 scale
-        gbytes_r = [float(n_keys[g].sum()) * (w.H // 64) * (w.Dl + 2 * w.Dr + 4) for g in gidx_r]
+        # algorithmic gather: every key of a query's set once per 64-head workgroup: a bf16
+        # workspace row + bf16 rope row, or an fp8 row + bf16 rope row + its fp32 scale
+        per_key = 2 * w.Dl + 2 * w.Dr if use_ws else w.Dl + 2 * w.Dr + 4
+        gbytes_r = [float(n_keys[g].sum()) * (w.H // 64) * per_key for g in gidx_r]
         gbs = float(np.mean([b / (t * 1e-3) / 1e9 for b, t in zip(gbytes_r, t_rank)]))
         out["gather"] = {"bytes_per_rank": [round(b) for b in gbytes_r], "GB/s": round(gbs, 1),
                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    if use_ws:
+        t_dq = float(np.mean([events[k][w.P + 3][0].elapsed_time(events[k][w.P + 3][1]) for k in range(args.steps)]))
+        dq_bytes = float(n_cache) * (w.Dl + 2 * w.Dl) + (n_cache + 63) // 64 * 4
+        out["dequant"] = {"ms": round(t_dq, 4), "GB/s": round(dq_bytes / (t_dq * 1e-3) / 1e9, 1),
+                          "kind": "fp8 cache -> bf16 workspace, once per step"}
+        out["config"]["sparse_kv_read"] = "bf16 workspace dequantised once per step"
+    elif sparse:
+        out["config"]["sparse_kv_read"] = "fp8 rows dequantised inside the sparse kernel"
     if select:
         t_sel = float(np.mean([events[k][w.P + 2][0].elapsed_time(events[k][w.P + 2][1]) for k in range(args.steps)]))
         n_scores = float(sum((pos_r[r].astype(np.int64) + 1).sum() for r in range(w.P)))

@@ -18,10 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libmla_pcp.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = ("mla_pcp_abi_version", "mla_pcp_last_error", "pcp_plan_sizes", "pcp_partition",
-            "pcp_kv_insert", "pcp_kv_insert_fp8", "sparse_topk_select", "mla_prefill_partial", "pcp_lse_merge")
+            "pcp_kv_insert", "pcp_kv_insert_fp8", "pcp_kv_dequant_fp8", "sparse_topk_select", "mla_prefill_partial",
+            "pcp_lse_merge")
 
 _lib = None
 
@@ -72,6 +73,8 @@ def load():
     lib.pcp_kv_insert.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i32, _i64, _p, _p, _p]
     lib.pcp_kv_insert_fp8.restype = ctypes.c_int
     lib.pcp_kv_insert_fp8.argtypes = [_p, _p, _p, _i32, _i32, _i32, _i64, _p, _p, _p, _p]
+    lib.pcp_kv_dequant_fp8.restype = ctypes.c_int
+    lib.pcp_kv_dequant_fp8.argtypes = [_p, _p, _i64, _i32, _p, _i32, _p, _p]
     lib.sparse_topk_select.restype = ctypes.c_int
     lib.sparse_topk_select.argtypes = [_p, _i64, _p, _i32, _i32, _p, _p]
     lib.mla_prefill_partial.restype = ctypes.c_int
@@ -150,6 +153,12 @@ def pcp_kv_insert_fp8(local_latent, local_rope, slot, T, D_latent, D_rope, N_kv,
     st = load().pcp_kv_insert_fp8(_ptr(local_latent), _ptr(local_rope), _ptr(slot), T, D_latent, D_rope, N_kv,
                                   _ptr(kv_latent), _ptr(kv_rope), _ptr(kv_scale), _stream(stream))
     _check(st, "pcp_kv_insert_fp8")
+
+
+def pcp_kv_dequant_fp8(kv_latent, kv_scale, N_kv, D_latent, blocks, n_blocks, ws, stream=None):
+    st = load().pcp_kv_dequant_fp8(_ptr(kv_latent), _ptr(kv_scale), N_kv, D_latent, _ptr(blocks), n_blocks, _ptr(ws),
+                                   _stream(stream))
+    _check(st, "pcp_kv_dequant_fp8")
 
 
 def sparse_topk_select(scores, ld, positions, T, k, topk_idx, stream=None):

@@ -153,8 +153,26 @@ mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* po
     return MLA_OK;
 }
 
-// The sparse kernel addresses KV rows through 32-bit buffer offsets: N_kv * 512 < 2^32.
+mla_status pcp_kv_dequant_fp8(const void* kv_latent, const float* kv_scale, int64_t N_kv, int32_t D_latent,
+                              const int32_t* blocks, int32_t n_blocks, void* ws, void* stream) {
+    if (N_kv < 0 || N_kv > INT32_MAX || n_blocks < 0)
+        return fail(MLA_ERR_INVALID_ARG, "pcp_kv_dequant_fp8: sizes out of range");
+    if (D_latent != 512 && D_latent != 64)
+        return fail(MLA_ERR_UNSUPPORTED, "pcp_kv_dequant_fp8: D_latent=%d unsupported (512, 64)", D_latent);
+    if (n_blocks == 0 || N_kv == 0) return MLA_OK;
+    if (!kv_latent || !kv_scale || !blocks || !ws) return fail(MLA_ERR_INVALID_ARG, "pcp_kv_dequant_fp8: null pointer");
+    if (!aligned16(kv_latent) || !aligned16(ws))
+        return fail(MLA_ERR_INVALID_ARG, "pcp_kv_dequant_fp8: buffers must be 16-byte aligned");
+    hipError_t e = launch_kv_dequant_fp8(kv_latent, kv_scale, N_kv, D_latent, blocks, n_blocks, ws,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "pcp_kv_dequant_fp8: %s", hipGetErrorString(e));
+    return MLA_OK;
+}
+
+// The sparse kernels address KV rows through 32-bit buffer offsets: N_kv * 512 < 2^32 for
+// fp8 rows, N_kv * 1024 < 2^32 for bf16 rows.
 constexpr int64_t kSparseMaxKv = (int64_t(1) << 23) - 1;
+constexpr int64_t kSparseMaxKvBf16 = (int64_t(1) << 22) - 1;
 
 mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
     if (!a) return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: null args");
@@ -179,12 +197,12 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: topk=%d outside 0..2048", a->topk);
         if (a->window < 0 || a->window > 4096)
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: window=%d outside 0..4096", a->window);
-        if (!big || a->kv_dtype != MLA_KV_FP8_E4M3 || a->H % 64 != 0)
-            return fail(MLA_ERR_UNSUPPORTED,
-                        "mla_prefill_partial: sparse path needs 512+64 dims, fp8 KV and H %% 64 == 0");
-        if (a->N_kv > kSparseMaxKv)
-            return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path takes at most %d KV rows",
-                        (int)kSparseMaxKv);
+        if (!big || a->H % 64 != 0)
+            return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path needs 512+64 dims and H %% 64 == 0");
+        const int64_t max_kv = a->kv_dtype == MLA_KV_FP8_E4M3 ? kSparseMaxKv : kSparseMaxKvBf16;
+        if (a->N_kv > max_kv)
+            return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path takes at most %d KV rows of this dtype",
+                        (int)max_kv);
     } else if (a->kv_dtype != MLA_KV_BF16) {
         return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: dense path takes bf16 KV");
     }
@@ -207,8 +225,9 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: fp8 KV needs kv_scale");
     if (!aligned16(a->q) || !aligned16(a->latent_kv) || !aligned16(a->rope_k) || !aligned16(a->o_partial))
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: q/KV/output must be 16-byte aligned");
-    hipError_t e = sparse ? launch_sparse_partial(*a, (hipStream_t)stream)
-                          : launch_dense_partial(*a, (hipStream_t)stream);
+    hipError_t e = !sparse ? launch_dense_partial(*a, (hipStream_t)stream)
+                   : a->kv_dtype == MLA_KV_FP8_E4M3 ? launch_sparse_partial(*a, (hipStream_t)stream)
+                                                    : launch_sparse_bf16_partial(*a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_prefill_partial: %s", hipGetErrorString(e));
     return MLA_OK;
 }

@@ -100,6 +100,18 @@ __device__ __forceinline__ int score_key(int side, int half, int i) {
     return 32 * side + 16 * (i >> 3) + kperm(8 * ((i >> 2) & 1) + 4 * half + (i & 3));
 }
 
+// Sets to -inf the scores s[i] whose tile key score_key(side, half, i) has a clear bit in
+// `bits`. score_key(side, half, i) = 32 side + half + off(i) with the constant
+// off(i) = 16 (i/8) + 4 (i%4) + 2 ((i/4)%2), so one shift per lane and constant bit tests do it.
+__device__ __forceinline__ void mask_keys(f32x16& s, uint64_t bits, int side, int half) {
+    const uint32_t w = (uint32_t)(bits >> (32 * side + half));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int off = 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1);
+        s[i] = (w >> off) & 1u ? s[i] : -INFINITY;
+    }
+}
+
 // Per-lane LDS offsets inside a tile (everything else is an immediate):
 //  * Q K^T reads: LDS row of score row l32, 8 elements at 8*half of each 16-wide k-block
 //    (latent offsets from the latent rows' base, rope offsets from the rope rows' base);
@@ -218,15 +230,18 @@ __device__ __forceinline__ void tile_compute(const char* kvl, const char* kvr, c
     // Element j of the lane's k-slice of a 16-key block is key
     // 16 kb + 8 (j/4) + 4 half + j%4: two transposing reads of 4 keys each.
     __builtin_amdgcn_sched_barrier(0);
-    const char* v_own = kvl + lo.v + (32 * side) * S::LAT_STRIDE;
-    const char* v_oth = kvl + lo.v + (32 * (side ^ 1)) * S::LAT_STRIDE;
+    // Byte offsets from the tile base, each read addressed by one offset from kvl (a chain of
+    // pointer steps would hide from alias analysis that the reads stay inside this tile's
+    // buffer, and the compiler would then wait for loads streaming into the other one).
+    const int v_own = lo.v + (32 * side) * S::LAT_STRIDE;
+    const int v_oth = lo.v + (32 * (side ^ 1)) * S::LAT_STRIDE;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {  // own key blocks first: the partner's P has time to arrive
 #pragma unroll
         for (int d = 0; d < NB0; ++d) {
-            const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * S::LAT_STRIDE + (side * NB0 + d) * 64;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * S::LAT_STRIDE));
+            const int o0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * S::LAT_STRIDE + (side * NB0 + d) * 64;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kvl + o0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kvl + (o0 + 2 * S::LAT_STRIDE)));
             const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             const bf16x8 b = kb == 0 ? pk[0] : kb == 1 ? pk[1] : kb == 2 ? po0 : po1;
             acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc_o[d], 0, 0, 0);

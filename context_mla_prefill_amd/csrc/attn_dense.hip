@@ -379,14 +379,17 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         constexpr int NM = NB0 * 4;
         constexpr int PA = NM < PV_AHEAD ? NM : PV_AHEAD;
         constexpr int NVB = PA + 1;
-        const char* v_own = kvt + v_off + (32 * side) * T::LAT_STRIDE;
-        const char* v_oth = kvt + v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
+        // Byte offsets from the tile base; every read is addressed by one offset from kvt (a
+        // chain of pointer steps hides from alias analysis that the reads stay inside this
+        // tile, and the compiler then waits for the next tile's loads in the middle of P V).
+        const int v_own = v_off + (32 * side) * T::LAT_STRIDE;
+        const int v_oth = v_off + (32 * (side ^ 1)) * T::LAT_STRIDE;
         s16x4 vlo[NVB], vhi[NVB];
         auto vread = [&](int m) {
             const int kb = m / NB0, d = m % NB0;
-            const char* p0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
-            vlo[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
-            vhi[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 2 * T::LAT_STRIDE));
+            const int o0 = (kb < 2 ? v_own : v_oth) + (16 * (kb & 1)) * T::LAT_STRIDE + (side * NB0 + d) * 64;
+            vlo[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kvt + o0));
+            vhi[m % NVB] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kvt + (o0 + 2 * T::LAT_STRIDE)));
         };
 #pragma unroll
         for (int m = 0; m < PA; ++m) vread(m);

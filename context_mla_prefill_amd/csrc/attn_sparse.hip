@@ -8,10 +8,8 @@
 // support", "vLLM Launch Arguments" (the layout is this library's: E4M3FN codes, one
 // fp32 scale per 64 packed rows, rope kept bf16).
 //
-// Key set of a query at position p (request-relative): the selected indices that lie in
-// [0, p] and outside the window, plus every window key [max(0, p-window+1), p]; a selected
-// index inside the window is counted once (the window supplies it). Selected indices must
-// be distinct; -1 (or anything outside [0, p]) is a pad.
+// The key set (selected indices plus window, counted once) and its tiles are described in
+// sparse_keys.h.
 //
 // Work decomposition: one workgroup per (token, 64 heads), i.e. the same 64 rows and wave
 // pairs as the dense kernel, running the same per-tile compute. A tile is 64 key slots:
@@ -24,15 +22,13 @@
 //     bf16_rne(fp32(e4m3) * scale[row/64]);
 //   * rope rows stream straight into the tile once every wave is done with the previous
 //     tile's Q K^T reads.
-#include "attn_core.h"
+#include "sparse_keys.h"
 
 namespace mla {
 namespace {
 
 using namespace attn;
 
-constexpr int MAX_TOPK = 2048;
-constexpr int MAX_WINDOW = 4096;
 constexpr int GATHER_LOADS = BN / 2 / 4 + 1;  // per wave and tile: latent loads (2 keys each) + 1 scale load
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -66,12 +62,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     __shared__ uint64_t tmask[2];            // valid-key bits per staging slot
     __shared__ Exchange ex;
 
-    // workgroup = (token, 64-head group, key split); splits of one row are adjacent
-    const int hg_count = H / BM;
-    const int ridx = (int)blockIdx.x / kv_splits;
-    const int split = (int)blockIdx.x - ridx * kv_splits;
-    const int tok = ridx / hg_count;
-    const int hg = ridx - tok * hg_count;
+    const SparseWork wk = sparse_work(H, kv_splits, cu, n_vrows, vrow_kv_start, positions, vrow_kv_len);
+    const int tok = wk.tok;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int pair = wave >> 1;
@@ -80,24 +72,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const int half = lane >> 5;
     const int l32 = lane & 31;
 
-    // virtual row of this token: last v with cu[v] <= tok
-    int lo_v = 0, hi_v = n_vrows;
-    while (hi_v - lo_v > 1) {
-        const int mid = (lo_v + hi_v) >> 1;
-        if (cu[mid] <= tok) lo_v = mid; else hi_v = mid;
-    }
-    const int64_t kv0 = vrow_kv_start[lo_v];
-    const int p = positions[tok];
-    // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
-    int key_lo = 0, key_hi = INT32_MAX;
+    const int64_t kv0 = wk.kv0;
     if (kv_splits > 1) {
-        const int n = (vrow_kv_len[lo_v] + BN - 1) / BN;
-        key_lo = BN * (int)((unsigned)split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
-        key_hi = BN * (int)((unsigned)(split + 1) * n / kv_splits);
-        o_out += split * split_stride * H * DL;
-        lse_out += split * split_stride * H;
+        o_out += wk.split * split_stride * H * DL;
+        lse_out += wk.split * split_stride * H;
     }
-    const int head = hg * BM + pair * 32 + l32;
+    const int head = wk.hg * BM + pair * 32 + l32;
     const int64_t grow = (int64_t)tok * H + head;
     // Keys are addressed by row relative to row_base: the request's first row for packed KV
     // (row = key position), 0 for paged KV (row = block_table entry * 64 + position % 64).
@@ -111,25 +91,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         (void*)(rope + row_base * (DR * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DR * 2)), kBufferFlags);
     const __amdgpu_buffer_rsrc_t scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)kv_scale, 0, (int)(uint32_t)(((N_kv + 63) / 64) * 4), kBufferFlags);
-    const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[lo_v] * bt_stride : nullptr;
-    // Empty slots read the row of key 0 (a written key of the request: its value meets a
-    // zero probability, so it must be finite).
-    const int pad_row = PAGED ? bt_row[0] * BN : 0;
-    const int win_lo = max(0, p - window + 1);  // first window key (window > 0)
-
-    // The selected indices, filtered once: an entry outside [0, p], outside this split's key
-    // range or inside the window (which supplies it) becomes -1; a kept one becomes its row.
-    for (int i = tid; i < MAX_TOPK; i += NT) {
-        const int e = i < topk ? topk_idx[(int64_t)tok * topk + i] : -1;
-        const bool ok = e >= key_lo && e < key_hi && e <= p && (window == 0 || e < win_lo);
-        int r = -1;
-        if (ok) r = PAGED ? bt_row[e >> 6] * BN + (e & (BN - 1)) : e;
-        sel[i] = r;
-    }
-    if constexpr (PAGED) {
-        const int nwb = window > 0 ? (p >> 6) - (win_lo >> 6) + 1 : 0;  // <= MAX_WINDOW / BN + 1
-        for (int i = tid; i < nwb; i += NT) win_blk[i] = bt_row[(win_lo >> 6) + i];
-    }
+    const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[wk.lo_v] * bt_stride : nullptr;
+    const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row);
 
     bf16x8 qf[S::KB];
     {
@@ -139,32 +102,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     }
     __syncthreads();
 
-    const int n_sel_tiles = (topk + BN - 1) / BN;
-    const int n_tiles = n_sel_tiles + (window + BN - 1) / BN;
-
-    // Row (relative to row_base) of the key in slot j of tile t and whether the slot holds a
-    // key of the set; empty slots and tiles past the last one read pad_row.
-    auto slot_key = [&](int t, int j, bool& ok) -> int {
-        if (t < n_sel_tiles) {
-            const int e = sel[t * BN + j];
-            ok = e >= 0;
-            return ok ? e : pad_row;
-        }
-        const int w = (t - n_sel_tiles) * BN + j;
-        const int k = win_lo + w;
-        ok = window > 0 && w < window && k <= p && k >= key_lo && k < key_hi;
-        if (!ok) return pad_row;
-        return PAGED ? win_blk[(k >> 6) - (win_lo >> 6)] * BN + (k & (BN - 1)) : k;
-    };
-    // Next tile index >= t that holds at least one key (n_tiles if none); workgroup-uniform.
-    auto next_live = [&](int t) -> int {
-        for (; t < n_tiles; ++t) {
-            bool ok = false;
-            if (lane < BN) slot_key(t, lane, ok);
-            if (__ballot(ok)) break;  // every wave evaluates the same slots
-        }
-        return t;
-    };
+    const int n_tiles = ks.n_tiles;
+    auto slot_key = [&](int t, int j, bool& ok) -> int { return ks.slot_key(t, j, ok); };
+    auto next_live = [&](int t) -> int { return ks.next_live(t, lane); };
     // Gathers tile t into staging slot b: fp8 latent rows (wave-wide load n moves keys 2n and
     // 2n+1, 32 lanes x 16 bytes each), the 64-row scale of each key (wave w: keys 16w..16w+15)
     // and the valid-key bits. Every wave issues exactly GATHER_LOADS loads.
@@ -262,10 +202,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         const uint64_t bits = tmask[b];
         __syncthreads();  // bf16 tile complete; staging slot b free
         const int tnn = tn < n_tiles ? next_live(tn + 1) : n_tiles;
-        auto keymask = [&](f32x16& s) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = (bits >> score_key(side, half, i)) & 1 ? s[i] : -INFINITY;
-        };
+        auto keymask = [&](f32x16& s) { mask_keys(s, bits, side, half); };
         auto prefetch = [&] {  // after every wave's Q K^T reads of tile t
             if (tn < n_tiles) gather_rope(tn);
             gather_latent(tnn, b);

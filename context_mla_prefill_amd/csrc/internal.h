@@ -35,10 +35,14 @@ hipError_t launch_kv_insert_fp8(const void* local_latent, const void* local_rope
                                 int32_t T, int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent,
                                 void* kv_rope, float* kv_scale, hipStream_t stream);
 
+hipError_t launch_kv_dequant_fp8(const void* kv_latent, const float* kv_scale, int64_t N_kv, int32_t D_latent,
+                                 const int32_t* blocks, int32_t n_blocks, void* ws, hipStream_t stream);
+
 hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* positions, int32_t T, int32_t k,
                               int32_t* topk_idx, hipStream_t stream);
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream);
+hipError_t launch_sparse_bf16_partial(const mla_partial_args& a, hipStream_t stream);
 
 }  // namespace mla

@@ -123,7 +123,56 @@ hipError_t launch_fp8_insert(const void* local_latent, const void* local_rope, c
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Dequantise listed 64-row blocks of an fp8-e4m3 latent cache into a bf16 workspace with the
+// cache's row addressing: ws[r] = bf16_rne(fp32(e4m3(code[r])) * scale[r / 64]), the same
+// arithmetic (and instructions) as the sparse kernel's in-tile dequantisation. One workgroup
+// per block; a thread turns 16 codes (16 bytes) into 16 bf16 values (32 bytes) per step.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int DL>
+__global__ __launch_bounds__(256) void fp8_dequant_blocks(const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scale,
+                                                          const int32_t* __restrict__ blocks, int64_t N_kv,
+                                                          __bf16* __restrict__ ws) {
+    const int64_t blk = blocks[blockIdx.x];
+    if (blk < 0 || blk * 64 >= N_kv) return;  // workgroup-uniform
+    const float sc = scale[blk];
+    constexpr int CH = DL / 16;  // 16-byte chunks per row
+    for (int k = threadIdx.x; k < 64 * CH; k += 256) {
+        const int64_t r = blk * 64 + k / CH;
+        if (r >= N_kv) break;  // rows past the cache end: the rest of this thread's chunks too
+        const int c = k % CH;
+        const uint4 raw = *reinterpret_cast<const uint4*>(codes + r * DL + c * 16);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        bf16x8 o[2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[q], true);
+            o[q >> 1][4 * (q & 1) + 0] = (__bf16)(a.x * sc);
+            o[q >> 1][4 * (q & 1) + 1] = (__bf16)(a.y * sc);
+            o[q >> 1][4 * (q & 1) + 2] = (__bf16)(b.x * sc);
+            o[q >> 1][4 * (q & 1) + 3] = (__bf16)(b.y * sc);
+        }
+        bf16x8* dst = reinterpret_cast<bf16x8*>(ws + r * DL + c * 16);
+        dst[0] = o[0];
+        dst[1] = o[1];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_kv_dequant_fp8(const void* kv_latent, const float* kv_scale, int64_t N_kv, int32_t D_latent,
+                                 const int32_t* blocks, int32_t n_blocks, void* ws, hipStream_t stream) {
+    if (D_latent == 512)
+        hipLaunchKernelGGL((fp8_dequant_blocks<512>), dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                           (const uint8_t*)kv_latent, kv_scale, blocks, N_kv, (__bf16*)ws);
+    else
+        hipLaunchKernelGGL((fp8_dequant_blocks<64>), dim3((unsigned)n_blocks), dim3(256), 0, stream,
+                           (const uint8_t*)kv_latent, kv_scale, blocks, N_kv, (__bf16*)ws);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_insert_fp8(const void* local_latent, const void* local_rope, const int32_t* slot, int32_t T,
                                 int32_t D_latent, int32_t D_rope, int64_t N_kv, void* kv_latent, void* kv_rope,

@@ -1,0 +1,127 @@
+// Key sets of the sparse partial attention, shared by its fp8 and bf16 kernels.
+//
+// Key set of a query at position p (request-relative): the selected indices that lie in
+// [0, p] and outside the window, plus every window key [max(0, p-window+1), p]; a selected
+// index inside the window is counted once (the window supplies it). Selected indices must be
+// distinct; -1 (or anything outside [0, p]) is a pad. With split KV only keys in the split's
+// range [key_lo, key_hi) count. ("[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid
+// KV and MegaMoE", "Purpose": sparse prefill attention under PCP.)
+//
+// A workgroup owns one token and 64 heads; its keys are visited in tiles of 64 slots: first the
+// selected indices in groups of 64, then the window.
+#pragma once
+
+#include "attn_core.h"
+
+namespace mla {
+namespace attn {
+
+constexpr int MAX_TOPK = 2048;
+constexpr int MAX_WINDOW = 4096;
+
+// The workgroup's token, head group and key split, its virtual row and the split's key range.
+struct SparseWork {
+    int tok, hg, split, lo_v, p, key_lo, key_hi;
+    int64_t kv0;
+};
+
+__device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const int32_t* __restrict__ cu, int n_vrows,
+                                                 const int32_t* __restrict__ vrow_kv_start,
+                                                 const int32_t* __restrict__ positions,
+                                                 const int32_t* __restrict__ vrow_kv_len) {
+    SparseWork w;
+    // workgroup = (token, 64-head group, key split); splits of one row are adjacent
+    const int hg_count = H / BM;
+    const int ridx = (int)blockIdx.x / kv_splits;
+    w.split = (int)blockIdx.x - ridx * kv_splits;
+    w.tok = ridx / hg_count;
+    w.hg = ridx - w.tok * hg_count;
+    // virtual row of this token: last v with cu[v] <= tok
+    int lo_v = 0, hi_v = n_vrows;
+    while (hi_v - lo_v > 1) {
+        const int mid = (lo_v + hi_v) >> 1;
+        if (cu[mid] <= w.tok) lo_v = mid; else hi_v = mid;
+    }
+    w.lo_v = lo_v;
+    w.kv0 = vrow_kv_start[lo_v];
+    w.p = positions[w.tok];
+    // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
+    w.key_lo = 0;
+    w.key_hi = INT32_MAX;
+    if (kv_splits > 1) {
+        const int n = (vrow_kv_len[lo_v] + BN - 1) / BN;
+        w.key_lo = BN * (int)((unsigned)w.split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
+        w.key_hi = BN * (int)((unsigned)(w.split + 1) * n / kv_splits);
+    }
+    return w;
+}
+
+// Rows of the keys: relative to the request's first row for packed KV (row = key position),
+// absolute for paged KV (row = block_table entry * 64 + position % 64).
+template <bool PAGED>
+struct SparseKeys {
+    const int* sel;      // LDS [MAX_TOPK]: row of each selected key of the set, -1 otherwise
+    const int* win_blk;  // LDS: paged cache blocks the window spans
+    int n_sel_tiles, n_tiles, window, win_lo, p, key_lo, key_hi, pad_row;
+
+    // Row of the key in slot j of tile t and whether the slot holds a key of the set; empty
+    // slots and tiles past the last one read pad_row (the row of key 0: a written key whose
+    // value meets a zero probability, so it must be finite).
+    __device__ __forceinline__ int slot_key(int t, int j, bool& ok) const {
+        if (t < n_sel_tiles) {
+            const int e = sel[t * BN + j];
+            ok = e >= 0;
+            return ok ? e : pad_row;
+        }
+        const int w = (t - n_sel_tiles) * BN + j;
+        const int k = win_lo + w;
+        ok = window > 0 && w < window && k <= p && k >= key_lo && k < key_hi;
+        if (!ok) return pad_row;
+        return PAGED ? win_blk[(k >> 6) - (win_lo >> 6)] * BN + (k & (BN - 1)) : k;
+    }
+    // Next tile index >= t that holds at least one key (n_tiles if none); workgroup-uniform.
+    __device__ __forceinline__ int next_live(int t, int lane) const {
+        for (; t < n_tiles; ++t) {
+            bool ok = false;
+            if (lane < BN) slot_key(t, lane, ok);
+            if (__ballot(ok)) break;  // every wave evaluates the same slots
+        }
+        return t;
+    }
+};
+
+// Fills the workgroup's selected-row list and window blocks (all threads take part; a barrier
+// must follow before slot_key is used). The selected indices are filtered once: an entry
+// outside [0, p], outside the split's key range or inside the window becomes -1, a kept one
+// its row.
+template <bool PAGED>
+__device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk, const int32_t* __restrict__ topk_idx,
+                                                         int topk, int window, const SparseWork& w,
+                                                         const int32_t* __restrict__ bt_row) {
+    SparseKeys<PAGED> ks;
+    ks.sel = sel;
+    ks.win_blk = win_blk;
+    ks.window = window;
+    ks.p = w.p;
+    ks.key_lo = w.key_lo;
+    ks.key_hi = w.key_hi;
+    ks.win_lo = max(0, w.p - window + 1);  // first window key (window > 0)
+    ks.pad_row = PAGED ? bt_row[0] * BN : 0;
+    ks.n_sel_tiles = (topk + BN - 1) / BN;
+    ks.n_tiles = ks.n_sel_tiles + (window + BN - 1) / BN;
+    for (int i = threadIdx.x; i < MAX_TOPK; i += NT) {
+        const int e = i < topk ? topk_idx[(int64_t)w.tok * topk + i] : -1;
+        const bool ok = e >= w.key_lo && e < w.key_hi && e <= w.p && (window == 0 || e < ks.win_lo);
+        int r = -1;
+        if (ok) r = PAGED ? bt_row[e >> 6] * BN + (e & (BN - 1)) : e;
+        sel[i] = r;
+    }
+    if constexpr (PAGED) {
+        const int nwb = window > 0 ? (w.p >> 6) - (ks.win_lo >> 6) + 1 : 0;  // <= MAX_WINDOW / BN + 1
+        for (int i = threadIdx.x; i < nwb; i += NT) win_blk[i] = bt_row[(ks.win_lo >> 6) + i];
+    }
+    return ks;
+}
+
+}  // namespace attn
+}  // namespace mla

@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-#define MLA_PCP_ABI_VERSION 4
+#define MLA_PCP_ABI_VERSION 5
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -158,6 +158,25 @@ mla_status pcp_kv_insert_fp8(const void* local_latent, const void* local_rope, c
                              void* kv_rope, float* kv_scale, void* stream);
 
 /*
+ * pcp_kv_dequant_fp8 — dequantise listed 64-row blocks of an fp8-e4m3 latent cache into a
+ * bf16 workspace with the same row addressing, once per step, for the sparse partial to read
+ * bf16 rows (the dequantised-workspace reuse of sparse BF16 CP prefill: "DeepSeek-V4.1: Prefill
+ * support CP with multistream forward prepare (4/N)", commit list, "Reuse shared compressed KV
+ * dequantization in V4.1 CP prefill").
+ * For every listed block B and row r in [64 B, 64 B + 64) with r < N_kv:
+ *   ws[r] = bf16_rne(fp32(e4m3(kv_latent[r])) * kv_scale[B])   (bit-identical to the sparse
+ *   partial's in-kernel dequantisation).
+ *  kv_latent  device uint8 [N_kv][D_latent]; kv_scale device fp32 [ceil(N_kv / 64)];
+ *  blocks     device int32 [n_blocks] block ids (ids outside the cache are skipped; a block
+ *             listed twice is written twice with the same bytes);
+ *  ws         device bf16 [N_kv][D_latent] (rows of unlisted blocks untouched).
+ * Errors: INVALID_ARG (null, sizes < 0, N_kv > 2^31 - 1, 16-byte misalignment); UNSUPPORTED
+ * (D_latent not 64 / 512); HIP.
+ */
+mla_status pcp_kv_dequant_fp8(const void* kv_latent, const float* kv_scale, int64_t N_kv, int32_t D_latent,
+                              const int32_t* blocks, int32_t n_blocks, void* ws, void* stream);
+
+/*
  * sparse_topk_select — per query row, the k key positions of its causal prefix with the
  * largest index scores: the selected-index input of the sparse partial (the indexer's top-k
  * ahead of sparse MLA, "DeepSeek-V4.1: Prefill support CP with multistream forward prepare
@@ -197,7 +216,8 @@ mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* po
  *   S_j = scale * <q[i][h], key_j>; O = softmax(S) @ latent (bf16, round to nearest
  *   even); LSE = log(sum_j exp(S_j)) (fp32, natural log). No sink.
  * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]) (row = KV row, so
- *   with paging one scale per block).
+ *   with paging one scale per block), dequantised inside the sparse kernel. A sparse call with
+ *   bf16 latent (for instance the workspace of pcp_kv_dequant_fp8) gathers bf16 rows instead.
  * Split KV (kv_splits = S > 1): the key set of a row is cut by key position into S
  *   ranges and each range gives its own partial (O, LSE), written at split slice s of
  *   the outputs; merging the S partials (pcp_lse_merge with the same S) gives the
@@ -244,8 +264,8 @@ typedef struct mla_partial_args {
  * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1,
  * block_table without vrow_req or with bt_stride < 1);
  * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
- * bf16 KV, with H not a multiple of 64 or with N_kv >= 2^23 rows, dense with fp8 KV,
- * dtype); HIP.
+ * dims other than 512+64, with H not a multiple of 64, with fp8 KV of N_kv >= 2^23 rows or
+ * bf16 KV of N_kv >= 2^22 rows (32-bit byte offsets), dense with fp8 KV, dtype); HIP.
  * Sparse preconditions: selected indices of a row are distinct; entries outside [0, p]
  * (including -1) are pads. */
 mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);

@@ -103,7 +103,10 @@ def test_partial_validation_errors():
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, H=64))[0] == _lib.MLA_ERR_INVALID_ARG  # no scale
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=16))[0] == _lib.MLA_ERR_UNSUPPORTED
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=96))[0] == _lib.MLA_ERR_UNSUPPORTED
-    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64))[0] == _lib.MLA_ERR_UNSUPPORTED  # bf16 sparse
+    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64, N_kv=1 << 22))[0] == \
+        _lib.MLA_ERR_UNSUPPORTED  # bf16 sparse rows addressed by 32-bit byte offsets
+    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64, D_latent=64, D_rope=16))[0] == \
+        _lib.MLA_ERR_UNSUPPORTED  # sparse needs 512+64
     assert call(_args(**ok, topk_idx=f, topk=64, window=5000, kv_dtype=1, kv_scale=f, H=64))[0] == \
         _lib.MLA_ERR_UNSUPPORTED
     assert call(_args(**ok, topk_idx=f, topk=64, window=128, kv_dtype=1, kv_scale=f, H=64, N_kv=1 << 23))[0] == \
@@ -151,6 +154,18 @@ def test_merge_and_insert_validation_errors():
     assert q8(kv_scale=None)[0] == _lib.MLA_ERR_INVALID_ARG
     assert q8(local_latent=_P(FAKE + 8))[0] == _lib.MLA_ERR_INVALID_ARG
     assert q8(T=0)[0] == 0
+
+
+def test_dequant_validation_errors():
+    f = _P(FAKE)
+    dq = lambda **kw: _status(lambda: _lib.pcp_kv_dequant_fp8(**{**dict(
+        kv_latent=f, kv_scale=f, N_kv=128, D_latent=512, blocks=f, n_blocks=2, ws=f, stream=0), **kw}))
+    assert dq(D_latent=128)[0] == _lib.MLA_ERR_UNSUPPORTED
+    assert dq(N_kv=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert dq(n_blocks=-1)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert dq(blocks=None)[0] == _lib.MLA_ERR_INVALID_ARG
+    assert dq(ws=_P(FAKE + 2))[0] == _lib.MLA_ERR_INVALID_ARG
+    assert dq(n_blocks=0)[0] == 0 and dq(N_kv=0)[0] == 0
 
 
 def test_topk_select_validation_errors():

@@ -232,7 +232,7 @@ class PagedSparseRun:
     """partition (paged) -> fp8 quantise-on-insert of context and new rows -> P sparse
     partials -> merge. The oracle quantises the same bf16 rows itself."""
 
-    def __init__(self, w, seed, kv_splits=1):
+    def __init__(self, w, seed, kv_splits=1, workspace=False):
         self.w, self.kv_splits = w, kv_splits
         self.plan = plan = hp.oracle_plan(w)
         print(f"[run] sparse paged {w.name} T={w.T_glob} kv_splits={kv_splits}", flush=True)
@@ -271,13 +271,22 @@ class PagedSparseRun:
                                                              ok.paged_rows(self.bt, req[g], pos[g]))
         self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
         self.sink_d = torch.from_numpy(self.sink).cuda()
+        if workspace:  # the batch's blocks dequantised once into a bf16 workspace
+            self.ws = torch.empty(N, w.Dl, dtype=torch.bfloat16, device="cuda")
+            used = np.unique(self.bt[self.bt >= 0]).astype(np.int32)
+            _lib.pcp_kv_dequant_fp8(self.codes_d, self.scales_d, N, w.Dl, torch.from_numpy(used).cuda(), len(used),
+                                    self.ws)
         for r, rp in enumerate(plan.ranks):
             gi = torch.from_numpy(rp.local_gidx.astype(np.int64)).cuda()
             ri = pp.RankInputs(q=q.index_select(0, gi).contiguous(), topk=topk_d.index_select(0, gi).contiguous(),
                                latent=None, rope=None)
-            args = pp.partial_args(pl, r, ri, self.codes_d, self.rope_d, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=self.scales_d, topk=w.topk,
-                                   window=w.window, kv_splits=kv_splits)
+            if workspace:
+                args = pp.partial_args(pl, r, ri, self.ws, self.rope_d, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                       topk=w.topk, window=w.window, kv_splits=kv_splits)
+            else:
+                args = pp.partial_args(pl, r, ri, self.codes_d, self.rope_d, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                       kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=self.scales_d, topk=w.topk,
+                                       window=w.window, kv_splits=kv_splits)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
@@ -325,3 +334,16 @@ def test_paged_sparse_quantize_on_insert(gpu_lib, seed):
     check_paged_plan(run.pl, run.plan, run.bt)
     run.check_cache()
     run.check_values()
+
+
+@pytest.mark.parametrize("seed", sorted(PAGED_SPARSE))
+def test_paged_sparse_workspace(gpu_lib, seed):
+    """The same paged batches with the quantised blocks dequantised once into a bf16
+    workspace: partials bit-identical to the in-kernel dequantisation."""
+    q, kv, P, topk, window, S = PAGED_SPARSE[seed]
+    w = synth.custom(seed, q, kv, P=P, H=64, Dl=512, Dr=64, topk=topk, window=window, latent_std=1.0)
+    fp8 = PagedSparseRun(w, seed, kv_splits=S)
+    ws = PagedSparseRun(w, seed, kv_splits=S, workspace=True)
+    assert torch.equal(ws.bufs.o_cat.view(torch.int16), fp8.bufs.o_cat.view(torch.int16))
+    assert torch.equal(ws.bufs.lse_cat.view(torch.int32), fp8.bufs.lse_cat.view(torch.int32))
+    ws.check_values()

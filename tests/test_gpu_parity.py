@@ -299,9 +299,12 @@ SPARSE_O_TOL = 3e-2
 class SparseRun:
     """partition -> fp8 insert -> P sparse partials -> merge for an fp8 top-k workload."""
 
-    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None, kv_splits=1):
+    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None, kv_splits=1, workspace=False):
+        """workspace: dequantise the cache once into a bf16 workspace (pcp_kv_dequant_fp8) and
+        run the sparse partials on bf16 rows instead of dequantising inside the kernel."""
         self.w = w
         self.kv_splits = kv_splits
+        self.workspace = workspace
         self.plan = hp.oracle_plan(w)
         print(f"[run] sparse workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
         self.q_bits = synth.q_rows(w)
@@ -328,10 +331,19 @@ class SparseRun:
         for r, ri in enumerate(ranks):
             _lib.pcp_kv_insert(ri.latent, ri.rope, pl.slot[pl.rank_rows(r)], pl.T_loc[r], w.Dl, w.Dr,
                                _lib.MLA_KV_FP8_E4M3, w.N_kv, self.kv_lat, self.kv_rope)
+        if workspace:
+            self.ws = torch.empty(w.N_kv, w.Dl, dtype=torch.bfloat16, device="cuda")
+            n_blk = (w.N_kv + 63) // 64
+            blocks = torch.arange(n_blk, dtype=torch.int32, device="cuda")
+            _lib.pcp_kv_dequant_fp8(self.kv_lat, scale_d, w.N_kv, w.Dl, blocks, n_blk, self.ws)
         for r, ri in enumerate(ranks):
-            args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                   kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk, window=w.window,
-                                   kv_splits=kv_splits)
+            if workspace:
+                args = pp.partial_args(pl, r, ri, self.ws, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                       topk=w.topk, window=w.window, kv_splits=kv_splits)
+            else:
+                args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
+                                       kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk,
+                                       window=w.window, kv_splits=kv_splits)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
@@ -509,6 +521,60 @@ def test_split_kv_sparse(gpu_lib):
     check_split_partials(run, sample, key_rows, SPARSE_O_TOL)
 
 
+def test_dequant_workspace_bit_exact(gpu_lib):
+    """pcp_kv_dequant_fp8 writes exactly the listed blocks, each row the oracle's
+    bf16_rne(fp32(e4m3) * scale) of every code (a partial last block, ids outside the cache
+    skipped, unlisted rows untouched)."""
+    rng = np.random.default_rng(77)
+    N, D = 64 * 5 + 17, 512
+    codes = rng.integers(0, 256, size=(N, D)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0  # no NaN codes
+    codes[0] = np.arange(512) % 256 & 0xFF
+    codes[0][(codes[0] & 0x7F) == 0x7F] = 0
+    scales = (rng.random(6) * 3 + 0.01).astype(np.float32)
+    blocks = np.array([0, 2, 5, 99, -1, 2], np.int32)
+    ws = torch.full((N, D), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    _lib.pcp_kv_dequant_fp8(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), N, D,
+                            torch.from_numpy(blocks).cuda(), len(blocks), ws)
+    torch.cuda.synchronize()
+    got = host_bits(ws)
+    for B in range(6):
+        rows = np.arange(64 * B, min(64 * B + 64, N))
+        if B in (0, 2, 5):
+            want = on.dequant_fp8_rows(codes[rows], rows, scales)
+            assert np.array_equal(on.bf16_to_f64(got[rows]), want), B
+        else:
+            assert np.all(got[rows] == 0x7FC0), B
+
+
+SPARSE_WS = {
+    # seed: (q_lens, kv_lens, P, H, topk, window, kv_splits)
+    221: ([1500, 700], [1500, 900], 2, 64, 256, 64, 1),
+    222: ([900, 1, 300], [900, 700, 300], 2, 128, 128, 32, 1),  # 2 head groups, a decode row
+    223: ([777], [1200], 2, 64, 64, 200, 3),                      # continuation, wide window, split KV
+}
+
+
+@pytest.mark.parametrize("seed", sorted(SPARSE_WS))
+def test_sparse_workspace_path(gpu_lib, seed):
+    """The sparse path on a bf16 workspace dequantised once (pcp_kv_dequant_fp8) gives the
+    same partials, bit for bit, as the in-kernel dequantisation, and matches the oracle."""
+    q, kv, P, H, topk, window, S = SPARSE_WS[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64, topk=topk, window=window, kv_dtype="fp8",
+                     latent_std=1.0)
+    fp8 = SparseRun(w, kv_splits=S)
+    ws = SparseRun(w, kv_splits=S, workspace=True)
+    assert torch.equal(ws.bufs.o_cat.view(torch.int16), fp8.bufs.o_cat.view(torch.int16))
+    assert torch.equal(ws.bufs.lse_cat.view(torch.int32), fp8.bufs.lse_cat.view(torch.int32))
+    if S == 1:
+        ws.check_values(np.arange(w.T_glob))
+    else:
+        toks = np.arange(w.T_glob)
+        ref = hp.oracle_sparse(w, ws.plan, ws.q_bits, ws.lat_codes, ws.kv_scale, ws.rope_bits, ws.topk, ws.sink,
+                               toks)
+        check_merged(ws, ref, toks, SPARSE_O_TOL)
+
+
 def test_sparse128k_p2_sampled(gpu_lib):
     """128K tokens, P=2, 64 heads, top-2048 + window 128, fp8 KV: plan and insert in full,
     values on the ends of every chunk plus random tokens, all rows finite."""
@@ -518,5 +584,16 @@ def test_sparse128k_p2_sampled(gpu_lib):
     run.check_insert()
     toks = hp.sample_tokens(w, run.plan, n_random=64)
     print(f"[check] sparse workload 4: {len(toks)} sampled tokens", flush=True)
+    run.check_values(toks)
+    assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())
+
+
+def test_sparse128k_p2_workspace_sampled(gpu_lib):
+    """The 128K top-2048 workload on the bf16 workspace path (the one the benchmark times):
+    sampled tokens against the oracle, all rows finite."""
+    w = synth.workload(4)
+    run = SparseRun(w, workspace=True)
+    toks = hp.sample_tokens(w, run.plan, n_random=64)
+    print(f"[check] sparse workload 4 on the workspace: {len(toks)} sampled tokens", flush=True)
     run.check_values(toks)
     assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())

@@ -135,13 +135,23 @@ struct LaneOffsets {
 //  mask(s):          applies -inf to scores of keys the row must not see (s[i] is tile
 //                    key score_key(side, half, i), for row l32);
 //  after_exchange(): runs right after the barrier that publishes the P fragments, when
-//                    every wave has finished its Q K^T reads of this tile.
-template <class S, int DL, class Mask, class Hook>
+//                    every wave has finished its Q K^T reads of this tile;
+//  issue(i):         (NLOADS > 0) issues vector-memory load i of NLOADS; the loads are
+//                    scheduled one after every LOAD_GAP-th Q K^T MFMA, so the vector memory
+//                    pipe drains them while the matrix core runs instead of stalling the wave
+//                    on a burst.
+struct NoLoads {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+constexpr int LOAD_GAP = 2;
+
+template <class S, int DL, int NLOADS = 0, class Mask, class Hook, class Issue = NoLoads>
 __device__ __forceinline__ void tile_compute(const char* kvl, const char* kvr, const bf16x8 (&qf)[S::KB],
                                              f32x16 (&acc_o)[S::NB / 2],
                                              float& m_ref, float& l_run, float scale_log2, int wave, int side,
                                              int lane, const LaneOffsets<S>& lo, Exchange& ex, Mask&& mask,
-                                             Hook&& after_exchange) {
+                                             Hook&& after_exchange, Issue&& issue = Issue{}) {
+    static_assert(NLOADS <= S::KB / LOAD_GAP, "loads fit among the Q K^T MFMAs");
     constexpr int NB0 = S::NB / 2;
     // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
     f32x16 s = f32x16{};
@@ -149,6 +159,8 @@ __device__ __forceinline__ void tile_compute(const char* kvl, const char* kvr, c
         const char* kl = kvl + lo.k_lat;
         const char* kr = kvr + lo.k_rope;
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NLOADS; ++i) issue(i);
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) {
             const char* ap = kb < DL / 16 ? kl + kb * 32 : kr + (kb - DL / 16) * 32;
@@ -162,6 +174,7 @@ __device__ __forceinline__ void tile_compute(const char* kvl, const char* kvr, c
         for (int kb = 0; kb < S::KB - AHEAD; ++kb) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (kb % LOAD_GAP == 0 && kb / LOAD_GAP < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
         __builtin_amdgcn_sched_barrier(0);

@@ -72,16 +72,15 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
 
     const int n_tiles = ks.n_tiles;
     // Latent rows of tile t into buffer dst: wave w loads slots 16w .. 16w+15, one row each;
-    // lane l of the wave first looks up slot 16w + l%16, the loads take the rows by readlane.
-    auto load_latent = [&](int t, char* dst) {
+    // lane l of the wave looks up slot 16w + l%16 (lat_rows), load n takes its row by readlane.
+    auto lat_rows = [&](int t) {
         bool ok;
-        const int row = min(ks.slot_key(t, LAT_PER_WAVE * wave + (lane & (LAT_PER_WAVE - 1)), ok), last_row);
-#pragma unroll
-        for (int n = 0; n < LAT_PER_WAVE; ++n) {
-            const uint32_t soff = (uint32_t)__builtin_amdgcn_readlane(row, n) * (DL * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(dst + (LAT_PER_WAVE * wave + n) * S::LAT_STRIDE),
-                                                     16, lane * 16, soff, 0, 0);
-        }
+        return min(ks.slot_key(t, LAT_PER_WAVE * wave + (lane & (LAT_PER_WAVE - 1)), ok), last_row);
+    };
+    auto lat_load = [&](int row, char* dst, int n) {
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readlane(row, n) * (DL * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(dst + (LAT_PER_WAVE * wave + n) * S::LAT_STRIDE),
+                                                 16, lane * 16, soff, 0, 0);
     };
     // Rope rows of tile t (7 rows of 144 bytes per load).
     auto load_rope = [&](int t) {
@@ -112,29 +111,32 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     int t = ks.next_live(0, lane);
     int tn = n_tiles;
     if (t < n_tiles) {
-        load_latent(t, kv_lat0);
+        const int row = lat_rows(t);
+#pragma unroll
+        for (int n = 0; n < LAT_PER_WAVE; ++n) lat_load(row, kv_lat0, n);
         load_rope(t);
         tn = ks.next_live(t + 1, lane);
     }
     // One tile: everything in flight is this tile's, so wait for all of it; then the next
-    // tile's latent rows stream into the other buffer during the compute, and its rope rows
-    // once every wave is past this tile's Q K^T.
+    // tile's latent rows stream into the other buffer during the compute (one load after every
+    // second Q K^T MFMA; past the last tile they load pad rows into the unused buffer), and its
+    // rope rows once every wave is past this tile's Q K^T.
     auto step = [&](const char* cur, char* nxt) {
         bool ok;
         ks.slot_key(t, lane, ok);
         const uint64_t bits = __ballot(ok);  // valid slots of tile t (every wave the same)
+        const int nrow = lat_rows(tn);
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t landed for this wave
         __syncthreads();                     // ... for every wave; buffer nxt is free
-        if (tn < n_tiles) load_latent(tn, nxt);
         const int tnn = tn < n_tiles ? ks.next_live(tn + 1, lane) : n_tiles;
         auto keymask = [&](f32x16& s) { mask_keys(s, bits, side, half); };
         auto rope_next = [&] {
             if (tn < n_tiles) load_rope(tn);
         };
-        tile_compute<S, DL>(cur, kv_rope, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex, keymask,
-                            rope_next);
+        tile_compute<S, DL, LAT_PER_WAVE>(cur, kv_rope, qf, acc_o, m_ref, l_run, scale_log2, wave, side, lane, lo, ex,
+                                          keymask, rope_next, [&](int n) { lat_load(nrow, nxt, n); });
         t = tn;
         tn = tnn;
     };

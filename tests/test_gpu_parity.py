@@ -429,6 +429,10 @@ def test_sparse_edge_cases(gpu_lib, seed):
     check_plan(run.pl, run.plan)
     run.check_insert()
     run.check_values(np.arange(w.T_glob))
+    # the same batch on the bf16 workspace: bit-identical partials
+    ws = SparseRun(w, topk_rows=rows, workspace=True)
+    assert torch.equal(ws.bufs.o_cat.view(torch.int16), run.bufs.o_cat.view(torch.int16))
+    assert torch.equal(ws.bufs.lse_cat.view(torch.int32), run.bufs.lse_cat.view(torch.int32))
 
 
 def split_ranges(L, S):

@@ -10,11 +10,12 @@
 // Per (token t, head h): M = max(s_h, max_k L_k), D = exp(s_h-M) + sum_k exp(L_k-M),
 // O = sum_k exp(L_k-M) O_k / D, LSE = M + log D, all in fp32; O stored bf16 (RNE).
 //
-// HBM-bound streaming: one workgroup per token. Its first threads turn the token's
-// contributor LSEs and the sinks into per-(contributor, head) weights in LDS; then the
-// whole workgroup streams the token's H*D_v output elements, 16 bytes per thread and
-// several vectors in flight, reading each contributor's rows (contiguous H*D_v bf16)
-// with full-width coalesced non-temporal loads (every byte is read exactly once).
+// HBM-bound streaming: one workgroup per (token, group of heads), a group being as many
+// whole heads as one round of loads covers (NT * UNROLL 16-byte vectors; 16 heads of 512).
+// Its first threads turn the token's contributor LSEs and the sinks into per-(contributor,
+// head) weights in LDS; then the workgroup streams the group's output elements, 16 bytes per
+// thread and UNROLL vectors in flight, reading each contributor's rows (contiguous bf16) with
+// full-width coalesced non-temporal loads (every byte is read exactly once).
 #include <math.h>
 
 #include "internal.h"
@@ -32,12 +33,15 @@ constexpr int UNROLL = 4;  // vectors per thread in flight
 
 __global__ __launch_bounds__(NT) void merge_kernel(
     const u32x4* __restrict__ o_cat, const float* __restrict__ lse_cat,
-    const int32_t* __restrict__ merge_src, int P, int S, int64_t split_stride, int H, int G, int64_t R_total,
+    const int32_t* __restrict__ merge_src, int P, int S, int64_t split_stride, int H, int G, int HG, int64_t R_total,
     const float* __restrict__ sink, u32x4* __restrict__ o_out, float* __restrict__ lse_out) {
     __shared__ int rows[MAXP];
     __shared__ int n_rows;
     __shared__ float wts[MAXP][MAXH];  // exp(L_k - M) / D per contributor and head
-    const int64_t t = blockIdx.x;
+    const int n_groups = (H + HG - 1) / HG;
+    const int64_t t = blockIdx.x / n_groups;
+    const int h_lo = (int)(blockIdx.x - t * n_groups) * HG;  // heads [h_lo, h_hi) of token t
+    const int h_hi = min(H, h_lo + HG);
     const int tid = threadIdx.x;
     if (tid == 0) {  // contributors: every rank's row, in each of its S split slices
         int n = 0;
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     }
     __syncthreads();
     const int n = n_rows;
-    for (int h = tid; h < H; h += NT) {
+    for (int h = h_lo + tid; h < h_hi; h += NT) {
         const float sig = sink ? sink[h] : -INFINITY;
         float M = sig;
         for (int k = 0; k < n; ++k) M = fmaxf(M, lse_cat[(int64_t)rows[k] * H + h]);
@@ -72,10 +76,11 @@ __global__ __launch_bounds__(NT) void merge_kernel(
         if (lse_out) lse_out[t * H + h] = M == -INFINITY ? -INFINITY : M + logf(D);
     }
     __syncthreads();
-    const int V = H * G;  // 16-byte vectors of this token's output
+    const int V = H * G;  // 16-byte vectors of a token's output
+    const int V_hi = h_hi * G;  // this group's vectors: [h_lo * G, V_hi)
     const u32x4* src_base = o_cat;
     u32x4* dst = o_out + t * V;
-    for (int v0 = tid; v0 < V; v0 += NT * UNROLL) {
+    for (int v0 = h_lo * G + tid; v0 < V_hi; v0 += NT * UNROLL) {
         float acc[UNROLL][8];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
@@ -87,12 +92,12 @@ __global__ __launch_bounds__(NT) void merge_kernel(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int v = v0 + u * NT;
-                raw[u] = v < V ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+                raw[u] = v < V_hi ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int v = v0 + u * NT;
-                const float w = v < V ? wts[k][v / G] : 0.0f;
+                const float w = v < V_hi ? wts[k][v / G] : 0.0f;
                 const bf16x8 x = __builtin_bit_cast(bf16x8, raw[u]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[u][j] += w * (float)x[j];
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int v = v0 + u * NT;
-            if (v < V) {
+            if (v < V_hi) {
                 bf16x8 y;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) y[j] = (__bf16)acc[u][j];
@@ -118,8 +123,10 @@ hipError_t launch_merge(const void* o_cat, const float* lse_cat, const int32_t* 
                         int32_t kv_splits, int64_t split_stride, const float* sink, void* o_out,
                         float* lse_out, hipStream_t stream) {
     const int G = D_v / 8;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)T_glob), dim3(NT), 0, stream, (const u32x4*)o_cat, lse_cat,
-                       merge_src, P, kv_splits, split_stride, H, G, R_total, sink, (u32x4*)o_out, lse_out);
+    const int HG = max(1, NT * UNROLL / G);  // heads per workgroup
+    const int64_t grid = T_glob * ((H + HG - 1) / HG);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, (const u32x4*)o_cat, lse_cat,
+                       merge_src, P, kv_splits, split_stride, H, G, HG, R_total, sink, (u32x4*)o_out, lse_out);
     return hipGetLastError();
 }
 

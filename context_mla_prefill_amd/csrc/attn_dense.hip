@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     int bw_base = 0, bw_v = 0;
     auto bw_load = [&](int base) {
         bw_base = base;
-        bw_v = bt_row[min(base + lane, nblk - 1)];
+        bw_v = bt_row[min(base + lane, min(nblk, bt_stride) - 1)];
     };
     // KV rows of tile kt (request-relative keys clamped to `last`).
     auto tile_rows = [&](int kt) -> TileRows {
@@ -291,7 +291,10 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         tr.rows = (int)min((int64_t)BN, last - tb + 1);
         if constexpr (PAGED) {
             const int t = (int)(tb >> 6);
-            tr.row0 = (int64_t)__builtin_amdgcn_readlane(bw_v, t - bw_base) * 64 + (tb & 63);
+            // block ids outside the cache are clamped into it (wrong values, never a stray access)
+            const int blk = min(max(__builtin_amdgcn_readlane(bw_v, t - bw_base), 0), (int)((N_kv - 1) >> 6));
+            tr.row0 = min((int64_t)blk * 64 + (tb & 63), N_kv - 1);
+            tr.rows = (int)max((int64_t)1, min((int64_t)tr.rows, N_kv - tr.row0));
             if (t == bw_base + 63) bw_load(bw_base + 64);
         } else {
             tr.row0 = kv0 + tb;

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     const __amdgpu_buffer_rsrc_t scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)kv_scale, 0, (int)(uint32_t)(((N_kv + 63) / 64) * 4), kBufferFlags);
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[wk.lo_v] * bt_stride : nullptr;
-    const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row);
+    const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row, bt_stride);
 
     bf16x8 qf[S::KB];
     {

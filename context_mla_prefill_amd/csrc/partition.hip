@@ -140,7 +140,8 @@ __global__ __launch_bounds__(256) void plan_tokens(
     const int pos = kv - q + i;
     // KV row of the token: packed after the request's first row, or through its block
     // (64 rows) in the block table
-    const int sl = block_table ? block_table[(int64_t)b * bt_stride + (pos >> 6)] * 64 + (pos & 63)
+    // (a table column past bt_stride, from a kv_len the table does not cover, reads its last entry)
+    const int sl = block_table ? block_table[(int64_t)b * bt_stride + min(pos >> 6, bt_stride - 1)] * 64 + (pos & 63)
                                : kv_start[b] + pos;
     // first virtual row of request b: lower bound of b in rank 0's vrow_req
     int vlo = 0, vhi = n_vrows;

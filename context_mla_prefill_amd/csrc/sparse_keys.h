@@ -97,7 +97,10 @@ struct SparseKeys {
 template <bool PAGED>
 __device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk, const int32_t* __restrict__ topk_idx,
                                                          int topk, int window, const SparseWork& w,
-                                                         const int32_t* __restrict__ bt_row) {
+                                                         const int32_t* __restrict__ bt_row, int bt_stride) {
+    // paged: table columns past bt_stride read its last entry; rows outside the cache are
+    // caught by the kernels' buffer views (wrong values, never a stray access)
+    auto blk = [&](int col) { return bt_row[min(col, bt_stride - 1)]; };
     SparseKeys<PAGED> ks;
     ks.sel = sel;
     ks.win_blk = win_blk;
@@ -106,19 +109,19 @@ __device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk,
     ks.key_lo = w.key_lo;
     ks.key_hi = w.key_hi;
     ks.win_lo = max(0, w.p - window + 1);  // first window key (window > 0)
-    ks.pad_row = PAGED ? bt_row[0] * BN : 0;
+    ks.pad_row = PAGED ? blk(0) * BN : 0;
     ks.n_sel_tiles = (topk + BN - 1) / BN;
     ks.n_tiles = ks.n_sel_tiles + (window + BN - 1) / BN;
     for (int i = threadIdx.x; i < MAX_TOPK; i += NT) {
         const int e = i < topk ? topk_idx[(int64_t)w.tok * topk + i] : -1;
         const bool ok = e >= w.key_lo && e < w.key_hi && e <= w.p && (window == 0 || e < ks.win_lo);
         int r = -1;
-        if (ok) r = PAGED ? bt_row[e >> 6] * BN + (e & (BN - 1)) : e;
+        if (ok) r = PAGED ? blk(e >> 6) * BN + (e & (BN - 1)) : e;
         sel[i] = r;
     }
     if constexpr (PAGED) {
         const int nwb = window > 0 ? (w.p >> 6) - (ks.win_lo >> 6) + 1 : 0;  // <= MAX_WINDOW / BN + 1
-        for (int i = threadIdx.x; i < nwb; i += NT) win_blk[i] = bt_row[(ks.win_lo >> 6) + i];
+        for (int i = threadIdx.x; i < nwb; i += NT) win_blk[i] = blk((ks.win_lo >> 6) + i);
     }
     return ks;
 }

@@ -171,6 +171,8 @@ EDGE = [
     (104, [130, 5, 1], [130, 5, 300], 4, 4, 64, 16),  # tiny dims, replicated rows
     (105, [64, 64], [64, 64], 2, 2, 64, 16),  # two requests, H = 2
     (106, [600, 1], [700, 900], 2, 64, 512, 64),  # H = 64
+    (108, [300, 1], [300, 500], 2, 128, 512, 64),  # H = 128 (the largest)
+    (109, [200, 50, 7], [200, 90, 7], 3, 3, 512, 64),  # H = 3: row tiles mix tokens of a virtual row
 ]
 
 

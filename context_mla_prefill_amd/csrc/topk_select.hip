@@ -30,7 +30,7 @@ constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int NW = NT / 64;
 constexpr int CAND = 6144;     // LDS candidates (4-byte key + 4-byte index each)
 constexpr int PER_THREAD = CAND / NT;
-constexpr int UNROLL = 8;      // float4 loads per thread and gather step (two steps in flight)
+constexpr int UNROLL = 4;      // float4 loads per thread and gather step (two steps in flight)
 constexpr int NSAMP = 2048;    // sampled scores for the threshold estimate
 constexpr int TILE = NT * 4;   // scores per ordered-pass step (4 consecutive per thread)
 
@@ -206,23 +206,38 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
         if ((int64_t)tid * 4 < n) load_step(v, (int64_t)tid * 4);
         for (int64_t b0 = (int64_t)tid * 4; b0 < n; b0 += UNROLL * TILE) {
             if (b0 + UNROLL * TILE < n) load_step(vn, b0 + UNROLL * TILE);
+            // this lane's takes among its 4 * UNROLL scores, then one slot range per wave: the
+            // lane's offset is a wave prefix sum of the take counts, bit plane by bit plane
+            uint32_t tm = 0;
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int64_t base = b0 + u * TILE;
                 const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t key = order_key(e4[e]);
-                    const bool take = base + e < n && key >= t0;
-                    const uint64_t bal = __ballot(take);
-                    if (bal == 0) continue;  // wave-uniform
-                    uint32_t slot0 = 0;
-                    if (lane == 0) slot0 = atomicAdd(&sh.count, (uint32_t)__popcll(bal));
-                    slot0 = __shfl(slot0, 0, 64);
-                    const uint32_t slot = slot0 + (uint32_t)__popcll(bal & ((1ull << lane) - 1));
-                    if (take && slot < CAND) {
-                        sh.key[slot] = key;
-                        sh.idx[slot] = (int32_t)(base + e);
+                for (int e = 0; e < 4; ++e)
+                    if (base + e < n && order_key(e4[e]) >= t0) tm |= 1u << (4 * u + e);
+            }
+            const uint32_t cnt = (uint32_t)__popc(tm);  // <= 32: six bit planes
+            uint32_t pre = 0, tot = 0;
+#pragma unroll
+            for (int bb = 0; bb < 6; ++bb) {
+                const uint64_t m = __ballot((cnt >> bb) & 1u);
+                pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << bb;
+                tot += (uint32_t)__popcll(m) << bb;
+            }
+            if (tot) {  // wave-uniform
+                uint32_t slot0 = 0;
+                if (lane == 0) slot0 = atomicAdd(&sh.count, tot);  // lane 0 is active whenever any lane is
+                uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot0) + pre;
+#pragma unroll
+                for (int q = 0; q < 4 * UNROLL; ++q) {
+                    if ((tm >> q) & 1u) {
+                        if (slot < CAND) {
+                            const float4 vq = v[q >> 2];
+                            sh.key[slot] = order_key((q & 3) == 0 ? vq.x : (q & 3) == 1 ? vq.y : (q & 3) == 2 ? vq.z : vq.w);
+                            sh.idx[slot] = (int32_t)(b0 + (q >> 2) * TILE + (q & 3));
+                        }
+                        ++slot;
                     }
                 }
             }

@@ -153,7 +153,10 @@ __device__ uint32_t select_rank(KeyAt key_at, int64_t count, uint32_t& rank, uin
     return prefix;
 }
 
-__global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
+// Six waves per SIMD (three workgroups per CU, as many as the LDS allows): the register cap
+// this sets (80 VGPRs) costs a few values parked in scratch between the prologue and the output
+// phase, outside the streaming loop, and hides far more memory latency than it costs.
+__global__ __launch_bounds__(NT, 6) void topk_select_kernel(const float* __restrict__ scores, int64_t ld,
                                                          const int32_t* __restrict__ positions, int k,
                                                          int32_t* __restrict__ out) {
     __shared__ Shared sh;

@@ -28,7 +28,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;
 constexpr int MAXP = 64;
-constexpr int MAXH = 128;
 constexpr int UNROLL = 4;  // vectors per thread in flight
 
 __global__ __launch_bounds__(NT) void merge_kernel(
@@ -37,7 +36,10 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     const float* __restrict__ sink, u32x4* __restrict__ o_out, float* __restrict__ lse_out) {
     __shared__ int rows[MAXP];
     __shared__ int n_rows;
-    __shared__ float wts[MAXP][MAXH];  // exp(L_k - M) / D per contributor and head
+    // exp(L_k - M) / D per contributor and head, [P * S][H] floats in dynamic LDS sized by the
+    // launch (a few hundred bytes for 4 ranks of 16 heads, so many workgroups share a CU)
+    extern __shared__ float wts_dyn[];
+    auto wts = [&](int k, int h) -> float& { return wts_dyn[k * H + h]; };
     const int n_groups = (H + HG - 1) / HG;
     const int64_t t = blockIdx.x / n_groups;
     const int h_lo = (int)(blockIdx.x - t * n_groups) * HG;  // heads [h_lo, h_hi) of token t
@@ -62,17 +64,17 @@ __global__ __launch_bounds__(NT) void merge_kernel(
         float M = sig;
         for (int k = 0; k < n; ++k) M = fmaxf(M, lse_cat[(int64_t)rows[k] * H + h]);
         float D = 0.0f;
-        for (int k = 0; k < n; ++k) wts[k][h] = 0.0f;
+        for (int k = 0; k < n; ++k) wts(k, h) = 0.0f;
         if (M != -INFINITY) {
             D = sig == -INFINITY ? 0.0f : expf(sig - M);
             for (int k = 0; k < n; ++k) {
                 const float w = expf(lse_cat[(int64_t)rows[k] * H + h] - M);
-                wts[k][h] = w;
+                wts(k, h) = w;
                 D += w;
             }
         }
         const float inv = D > 0.0f ? 1.0f / D : 0.0f;
-        for (int k = 0; k < n; ++k) wts[k][h] *= inv;
+        for (int k = 0; k < n; ++k) wts(k, h) *= inv;
         if (lse_out) lse_out[t * H + h] = M == -INFINITY ? -INFINITY : M + logf(D);
     }
     __syncthreads();
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int v = v0 + u * NT;
-                const float w = v < V_hi ? wts[k][v / G] : 0.0f;
+                const float w = v < V_hi ? wts(k, v / G) : 0.0f;
                 const bf16x8 x = __builtin_bit_cast(bf16x8, raw[u]);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[u][j] += w * (float)x[j];
@@ -125,7 +127,8 @@ hipError_t launch_merge(const void* o_cat, const float* lse_cat, const int32_t* 
     const int G = D_v / 8;
     const int HG = max(1, NT * UNROLL / G);  // heads per workgroup
     const int64_t grid = T_glob * ((H + HG - 1) / HG);
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, (const u32x4*)o_cat, lse_cat,
+    const size_t wts_bytes = (size_t)min(P * kv_splits, MAXP) * H * sizeof(float);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)grid), dim3(NT), wts_bytes, stream, (const u32x4*)o_cat, lse_cat,
                        merge_src, P, kv_splits, split_stride, H, G, HG, R_total, sink, (u32x4*)o_out, lse_out);
     return hipGetLastError();
 }

@@ -255,6 +255,48 @@ def test_merge_of_oracle_key_split_partials(gpu_lib, T, P):
         assert np.max(np.abs(got_o[t] - o)) < O_TOL and np.max(np.abs(lse_out[t].cpu().numpy() - l)) < LSE_TOL
 
 
+MERGE_SHAPES = [
+    # (D_v, H, P, kv_splits): head groups of a workgroup are 1024 / (D_v / 8) heads
+    (1024, 16, 2, 1),  # 8 heads per group, two groups
+    (136, 5, 4, 1),    # odd sizes: 60 heads per group, one partial group
+    (8, 128, 3, 2),    # one group of 128 heads, split slices
+    (512, 64, 2, 3),   # the sparse workload's heads with three split slices
+]
+
+
+@pytest.mark.parametrize("Dv,H,P,S", MERGE_SHAPES)
+def test_merge_shapes(gpu_lib, Dv, H, P, S):
+    """The merge over head groups and split slices against the oracle merge, with 0..P
+    contributing ranks per token (none: O = 0, LSE = sink) and some empty partials."""
+    rng = np.random.default_rng(Dv + 7 * H + 31 * P + S)
+    T = 37
+    stride = T * P  # rows from one split slice to the next
+    R = S * stride
+    o_bits = synth.bf16_bits((rng.standard_normal((R, H, Dv)) * 0.5).astype(np.float32))
+    lse = (rng.standard_normal((R, H)) * 3).astype(np.float32)
+    lse[rng.random((R, H)) < 0.05] = -np.inf  # a partial with no key
+    src = np.full((T, P), -1, np.int32)
+    for t in range(T):
+        for r in rng.permutation(P)[:int(rng.integers(0, P + 1))]:
+            src[t, r] = t * P + r
+    sink = rng.standard_normal(H).astype(np.float32)
+    o_out = torch.empty(T, H, Dv, dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    _lib.pcp_lse_merge(dev_bf16(o_bits), torch.from_numpy(lse).cuda(), torch.from_numpy(src).cuda(), P, T, H, Dv, R,
+                       torch.from_numpy(sink).cuda(), o_out, lse_out, kv_splits=S, split_stride=stride)
+    torch.cuda.synchronize()
+    # the contributors the API defines: every rank's row in each split slice
+    src_x = np.full((T, P * S), -1, np.int64)
+    for t in range(T):
+        for k in range(P):
+            if src[t, k] >= 0:
+                for sl in range(S):
+                    src_x[t, k * S + sl] = src[t, k] + sl * stride
+    want_o, want_l = om.merge(on.bf16_to_f64(o_bits), lse.astype(np.float64), src_x, sink.astype(np.float64))
+    np.testing.assert_allclose(on.bf16_to_f64(host_bits(o_out)), want_o, atol=4e-3, rtol=1e-2)
+    np.testing.assert_allclose(lse_out.cpu().numpy(), want_l, atol=1e-5, rtol=1e-6)
+
+
 def _sampled_run(cfg, n_random):
     w = synth.workload(cfg)
     run = DenseRun(w)

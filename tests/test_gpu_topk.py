@@ -73,6 +73,24 @@ def test_topk_select_edge_rows(gpu_lib, k):
             f"{np.nonzero(got[i] != want)[0][:5]}"
 
 
+def test_topk_select_rows_past_the_bitmap(gpu_lib):
+    """Rows longer than the LDS bitmap covers (more than 196,608 scores): the sampled threshold
+    and the LDS select, then the ordered pass over the row writes the indices."""
+    w = synth.workload(4)
+    ns = [196609, 200000, 250000, 262144]
+    ld = max(ns)
+    scores = synth.index_scores(w, [5, 6, 7, 8], ld)
+    scores[1, 100:3000] = 0.999999  # a long tie band near the top
+    pos = np.asarray(ns, np.int32) - 1
+    print(f"[run] top-k long rows {ns}", flush=True)
+    out = torch.empty(len(ns), 2048, dtype=torch.int32, device="cuda")
+    _lib.sparse_topk_select(torch.from_numpy(scores).cuda(), ld, torch.from_numpy(pos).cuda(), len(ns), 2048, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i, n in enumerate(ns):
+        assert np.array_equal(got[i], ot.topk_select(scores[i], n, 2048)), n
+
+
 def test_topk_select_full_size_sampled(gpu_lib):
     """One rank of the 128K top-2048 workload: 65536 query rows of up to 131072 hashed scores
     (34 GB). Every row checked for its invariants on the GPU (increasing, in the prefix, no

@@ -7,8 +7,8 @@ its real shape), and pcp_lse_merge. Default workload: one 131072-token request, 
 16 heads, latent 512 + rope 64 (bf16), per-head sink.
 
 Prints ONE JSON line. ``value`` is the attention TFLOP/s of the whole step
-(algorithmic flops of all ranks' partials / wall time of the step, inputs resident in
-HBM). ``roofline`` covers the dominant kernel (the partial attention), with its
+(algorithmic flops of every token's key set, each token counted once even where its row
+is replicated on every rank, / wall time of the step, inputs resident in HBM). ``roofline`` covers the dominant kernel (the partial attention), with its
 average launch time from HIP events on the launch stream. ``cpu_baseline`` times the
 fp64 oracle on a bounded sample of query rows of the same workload.
 
@@ -318,15 +318,22 @@ def main():
         n_keys = sparse_set_sizes(topk_host, w)
         gidx_r = [pl.local_gidx[pl.rank_rows(r)].cpu().numpy() for r in range(w.P)]
         flops_r = [float(2 * (w.Dl + w.Dr + w.Dl) * w.H) * float(n_keys[g].sum()) for g in gidx_r]
+        flops_step = float(2 * (w.Dl + w.Dr + w.Dl) * w.H) * float(n_keys.sum())
     else:
         flops_r = [attn_flops(p, w.H, w.Dl, w.Dr) for p in pos_r]
-    flops_step = float(sum(flops_r))
+        pos_glob = np.empty(w.T_glob, np.int64)
+        for r in range(w.P):
+            pos_glob[pl.local_gidx[pl.rank_rows(r)].cpu().numpy()] = pos_r[r]
+        flops_step = attn_flops(pos_glob, w.H, w.Dl, w.Dr)
+    # flops_r: what each rank's launch computes (rows replicated on every rank -- decode rows
+    # and short prefills -- count on each); flops_step: every global token once, the step's value
+    flops_launch = float(sum(flops_r))
     t_rank = [float(np.mean([events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)]))
               for r in range(w.P)]
     t_merge = float(np.mean([events[k][w.P][0].elapsed_time(events[k][w.P][1]) for k in range(args.steps)]))
     t_insert = float(np.mean([events[k][w.P + 1][0].elapsed_time(events[k][w.P + 1][1]) for k in range(args.steps)]))
     avg_launch_ms = float(np.mean(t_rank))
-    achieved = (flops_step / w.P) / (avg_launch_ms * 1e-3) / 1e12
+    achieved = (flops_launch / w.P) / (avg_launch_ms * 1e-3) / 1e12
     mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl, S)
     att_traffic, merge_traffic = measured_traffic(args.workload) if not args.paged else (None, None)
 

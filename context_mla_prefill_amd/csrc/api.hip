@@ -216,7 +216,10 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: too many workgroups");
     if (a->block_table && (!a->vrow_req || a->bt_stride < 1))
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: block_table needs vrow_req and bt_stride >= 1");
+    if (a->block_table && a->N_kv % 64 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: a paged cache holds whole 64-row blocks (N_kv %% 64 != 0)");
     if (a->T_loc == 0) return MLA_OK;
+    if (a->N_kv < 1) return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: T_loc > 0 with an empty KV cache");
     if (!a->q || !a->latent_kv || !a->rope_k || !a->cu_seqlens_q || !a->vrow_kv_start ||
         !a->positions || !a->o_partial || !a->lse)
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: null pointer");

@@ -279,10 +279,14 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     // read by v_readlane; the next 64 are fetched one tile before they are needed.
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[v] * bt_stride : nullptr;
     const int nblk = (int)(last >> 6) + 1;
+    // Block ids outside the cache are clamped into it as the window loads (wrong values, never
+    // a stray access); the cache holds whole blocks, so every tile -- one block, or the last key
+    // alone -- stays inside it.
+    const int blk_max = (int)(N_kv >> 6) - 1;
     int bw_base = 0, bw_v = 0;
     auto bw_load = [&](int base) {
         bw_base = base;
-        bw_v = bt_row[min(base + lane, min(nblk, bt_stride) - 1)];
+        bw_v = min(max(bt_row[min(base + lane, min(nblk, bt_stride) - 1)], 0), blk_max);
     };
     // KV rows of tile kt (request-relative keys clamped to `last`).
     auto tile_rows = [&](int kt) -> TileRows {
@@ -291,10 +295,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         tr.rows = (int)min((int64_t)BN, last - tb + 1);
         if constexpr (PAGED) {
             const int t = (int)(tb >> 6);
-            // block ids outside the cache are clamped into it (wrong values, never a stray access)
-            const int blk = min(max(__builtin_amdgcn_readlane(bw_v, t - bw_base), 0), (int)((N_kv - 1) >> 6));
-            tr.row0 = min((int64_t)blk * 64 + (tb & 63), N_kv - 1);
-            tr.rows = (int)max((int64_t)1, min((int64_t)tr.rows, N_kv - tr.row0));
+            tr.row0 = (int64_t)__builtin_amdgcn_readlane(bw_v, t - bw_base) * 64 + (tb & 63);
             if (t == bw_base + 63) bw_load(bw_base + 64);
         } else {
             tr.row0 = kv0 + tb;

@@ -250,7 +250,8 @@ typedef struct mla_partial_args {
     int32_t D_latent;            /* 512 (or 64)                                            */
     int32_t D_rope;              /* 64 (or 16)                                             */
     int32_t kv_dtype;            /* MLA_KV_BF16 or MLA_KV_FP8_E4M3                         */
-    int64_t N_kv;                /* rows of latent_kv / rope_k                             */
+    int64_t N_kv;                /* rows of latent_kv / rope_k (>= 1 when T_loc > 0; a
+                                    multiple of 64 when paged: whole blocks)               */
     float scale;                 /* softmax scale                                          */
     void* o_partial;             /* device bf16 out [T_loc][H][D_latent] (split slice 0)  */
     float* lse;                  /* device fp32 out [T_loc][H] (split slice 0)             */
@@ -266,7 +267,8 @@ typedef struct mla_partial_args {
 
 /* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales,
  * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1,
- * block_table without vrow_req or with bt_stride < 1);
+ * block_table without vrow_req or with bt_stride < 1, paged N_kv not a multiple of 64,
+ * T_loc > 0 with N_kv == 0);
  * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
  * dims other than 512+64, with H not a multiple of 64, with fp8 KV of N_kv >= 2^23 rows or
  * bf16 KV of N_kv >= 2^22 rows (32-bit byte offsets), dense with fp8 KV, dtype); HIP.

@@ -117,6 +117,10 @@ def test_partial_validation_errors():
     assert call(_args(**ok, kv_splits=2, split_stride=3, vrow_kv_len=f))[0] == _lib.MLA_ERR_INVALID_ARG  # < T_loc
     assert call(_args(**ok, block_table=f, bt_stride=4))[0] == _lib.MLA_ERR_INVALID_ARG  # no vrow_req
     assert call(_args(**ok, block_table=f, bt_stride=0, vrow_req=f))[0] == _lib.MLA_ERR_INVALID_ARG
+    st, msg = call(_args(**ok, block_table=f, bt_stride=4, vrow_req=f))  # N_kv = 16: a partial block
+    assert st == _lib.MLA_ERR_INVALID_ARG and "64-row blocks" in msg
+    st, msg = call(_args(**{**ok, "N_kv": 0}))
+    assert st == _lib.MLA_ERR_INVALID_ARG and "empty KV" in msg
     st, msg = call(_args(**ok, D_rope=32))
     assert st == _lib.MLA_ERR_UNSUPPORTED and "dims" in msg
     # empty shard: nothing to do, OK without touching any pointer

@@ -189,26 +189,15 @@ __global__ __launch_bounds__(NT, 6) void topk_select_kernel(const float* __restr
         __syncthreads();
         uint32_t j = (uint32_t)min((int64_t)NSAMP, max((int64_t)1, (int64_t)(k + CAND) / 2 * NSAMP / n));
         const uint32_t t0 = select_rank<true>([&](int64_t i) { return sh.key[i]; }, NSAMP, j, equal, sh);
-        // 2. gather keys >= t0 (slots by a wave-aggregated counter); the loads of the next step
-        //    are issued before the current one is processed
-        auto load_step = [&](float4 (&v)[UNROLL], int64_t b0) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int64_t base = b0 + u * TILE;
-                if (base + 4 <= n) {
-                    v[u] = *reinterpret_cast<const float4*>(srow + base);
-                } else {
-                    v[u].x = base < n ? srow[base] : -INFINITY;
-                    v[u].y = base + 1 < n ? srow[base + 1] : -INFINITY;
-                    v[u].z = base + 2 < n ? srow[base + 2] : -INFINITY;
-                    v[u].w = -INFINITY;
-                }
-            }
-        };
-        float4 v[UNROLL], vn[UNROLL];
-        if ((int64_t)tid * 4 < n) load_step(v, (int64_t)tid * 4);
-        for (int64_t b0 = (int64_t)tid * 4; b0 < n; b0 += UNROLL * TILE) {
-            if (b0 + UNROLL * TILE < n) load_step(vn, b0 + UNROLL * TILE);
+        // the score whose key is t0: for any score x (NaN aside), x >= f0 exactly when
+        // order_key(x) >= t0 (-0 >= +0 holds, as their keys are equal)
+        const float f0 = __uint_as_float((t0 & 0x80000000u) ? (t0 & 0x7FFFFFFFu) : ~t0);
+        // 2. gather keys >= t0 (slots by a wave-aggregated counter). The steps whose every score
+        //    lies in the row for every thread load unconditionally, the next step's loads issued
+        //    before the current step is processed: a static count in flight, so only the current
+        //    step's loads are waited for. The last, partial step follows them.
+        constexpr int64_t SU = UNROLL * TILE;
+        auto take = [&](const float4 (&v)[UNROLL], int64_t b0, bool full) {
             // this lane's takes among its 4 * UNROLL scores, then one slot range per wave: the
             // lane's offset is a wave prefix sum of the take counts, bit plane by bit plane
             uint32_t tm = 0;
@@ -218,7 +207,7 @@ __global__ __launch_bounds__(NT, 6) void topk_select_kernel(const float* __restr
                 const float e4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (base + e < n && order_key(e4[e]) >= t0) tm |= 1u << (4 * u + e);
+                    if ((full || base + e < n) && e4[e] >= f0) tm |= 1u << (4 * u + e);
             }
             const uint32_t cnt = (uint32_t)__popc(tm);  // <= 32: six bit planes
             uint32_t pre = 0, tot = 0;
@@ -244,8 +233,36 @@ __global__ __launch_bounds__(NT, 6) void topk_select_kernel(const float* __restr
                     }
                 }
             }
+        };
+        const int64_t n_full = n / SU;
+        auto load_full = [&](float4 (&d)[UNROLL], int64_t s) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                d[u] = *reinterpret_cast<const float4*>(srow + s * SU + u * TILE + (int64_t)tid * 4);
+        };
+        float4 v[UNROLL], vn[UNROLL];
+        if (n_full > 0) load_full(v, 0);
+        for (int64_t s = 0; s < n_full; ++s) {
+            load_full(vn, min(s + 1, n_full - 1));  // after the last full step: a repeat, unused
+            take(v, s * SU + (int64_t)tid * 4, true);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) v[u] = vn[u];
+        }
+        if (n_full * SU < n) {  // the partial step
+            const int64_t b0 = n_full * SU + (int64_t)tid * 4;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int64_t base = b0 + u * TILE;
+                if (base + 4 <= n) {
+                    v[u] = *reinterpret_cast<const float4*>(srow + base);
+                } else {
+                    v[u].x = base < n ? srow[base] : -INFINITY;
+                    v[u].y = base + 1 < n ? srow[base + 1] : -INFINITY;
+                    v[u].z = base + 2 < n ? srow[base + 2] : -INFINITY;
+                    v[u].w = -INFINITY;
+                }
+            }
+            take(v, b0, false);
         }
         __syncthreads();
         const uint32_t c = sh.count;

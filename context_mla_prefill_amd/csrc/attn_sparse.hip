@@ -113,12 +113,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         for (int i = 0; i < BN / 2 / 4; ++i) {
             const int n = i * 4 + wave;
             bool ok;
-            const int key = min(slot_key(t, 2 * n + half, ok), last_row);
+            const int key = max(min(slot_key(t, 2 * n + half, ok), last_row), 0);
             lds_dma16(lat_rsrc, (uint32_t)key * DL + l32 * 16, (char*)stage[b] + n * 1024);
         }
         {
             bool ok;
-            const int key = min(slot_key(t, 16 * wave + (lane & 15), ok), last_row);
+            const int key = max(min(slot_key(t, 16 * wave + (lane & 15), ok), last_row), 0);
             if (lane < 16)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(scale_rsrc, (lds_void*)&stage_scale[b][16 * wave], 4,
                                                          (uint32_t)((row_base + key) >> 6) * 4, 0, 0, 0);
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
             if (n >= S::ROPE_LOADS) break;  // wave-uniform
             const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
             bool ok;
-            const int key = min(slot_key(t, r < BN ? r : 0, ok), last_row);
+            const int key = max(min(slot_key(t, r < BN ? r : 0, ok), last_row), 0);
             if (ron && r < BN)
                 lds_dma16(rope_rsrc, (uint32_t)key * (DR * 2) + rc * 16, kv_rope + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
         }

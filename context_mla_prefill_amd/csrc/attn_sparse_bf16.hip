@@ -73,9 +73,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     const int n_tiles = ks.n_tiles;
     // Latent rows of tile t into buffer dst: wave w loads slots 16w .. 16w+15, one row each;
     // lane l of the wave looks up slot 16w + l%16 (lat_rows), load n takes its row by readlane.
+    // Rows are clamped into the cache before any offset is formed (a paged block id outside it
+    // reads a wrong row, never outside the cache): the latent row goes in the load's scalar
+    // offset, which the buffer range check does not cover, and no load relies on that check.
     auto lat_rows = [&](int t) {
         bool ok;
-        return min(ks.slot_key(t, LAT_PER_WAVE * wave + (lane & (LAT_PER_WAVE - 1)), ok), last_row);
+        return max(min(ks.slot_key(t, LAT_PER_WAVE * wave + (lane & (LAT_PER_WAVE - 1)), ok), last_row), 0);
     };
     auto lat_load = [&](int row, char* dst, int n) {
         const uint32_t soff = (uint32_t)__builtin_amdgcn_readlane(row, n) * (DL * 2);
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
             if (n >= S::ROPE_LOADS) break;  // wave-uniform
             const int r = n * S::ROPE_ROWS_PER_LOAD + rk;
             bool ok;
-            const int row = min(ks.slot_key(t, r < BN ? r : 0, ok), last_row);
+            const int row = max(min(ks.slot_key(t, r < BN ? r : 0, ok), last_row), 0);
             if (ron && r < BN)
                 lds_dma16(rope_rsrc, (uint32_t)row * (DR * 2) + rc * 16, kv_rope + n * S::ROPE_ROWS_PER_LOAD * S::ROPE_STRIDE);
         }

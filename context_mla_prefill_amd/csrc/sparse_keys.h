@@ -98,8 +98,9 @@ template <bool PAGED>
 __device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk, const int32_t* __restrict__ topk_idx,
                                                          int topk, int window, const SparseWork& w,
                                                          const int32_t* __restrict__ bt_row, int bt_stride) {
-    // paged: table columns past bt_stride read its last entry; rows outside the cache are
-    // caught by the kernels' buffer views (wrong values, never a stray access)
+    // paged: table columns past bt_stride read its last entry; the kernels clamp every row
+    // into the cache before they form an offset from it (a block id outside the cache gives
+    // wrong values, never a stray access)
     auto blk = [&](int col) { return bt_row[min(col, bt_stride - 1)]; };
     SparseKeys<PAGED> ks;
     ks.sel = sel;

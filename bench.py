@@ -131,6 +131,40 @@ def cpu_baseline(w, n_tokens: int, seconds: float):
                       f"fp64), {dt:.1f} s"}
 
 
+def box_reference(dev):
+    """Rates this box delivers outside the library, for context (timed after the step): a bf16
+    GEMM through torch.matmul (hipBLASLt), 8192^3, and a 1 GiB device-to-device copy."""
+    import torch
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return float(np.median(t))
+
+    t_gemm = timed(lambda: torch.matmul(a, b, out=c), 20)
+    del a, b, c
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    nbytes = src.numel() * 2
+    del src, dst
+    return {"gemm_bf16_tflops": round(2.0 * n ** 3 / (t_gemm * 1e-3) / 1e12, 1), "gemm": "torch.matmul bf16 8192^3",
+            "copy_GB/s": round(2.0 * nbytes / (t_copy * 1e-3) / 1e9, 1), "copy": "1 GiB device-to-device"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +184,8 @@ def main():
     ap.add_argument("--in-kernel-dequant", action="store_true",
                     help="top-k workload: the sparse kernel dequantises the fp8 rows of every tile itself, instead "
                          "of reading a bf16 workspace that pcp_kv_dequant_fp8 fills once per step")
+    ap.add_argument("--no-box-reference", action="store_true",
+                    help="skip the on-box bf16 GEMM and device-copy reference rates")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device-to-device copy three times "
                          "(a kernel of known byte count for scaling HBM traffic counters)")
@@ -328,8 +364,8 @@ def main():
     # flops_r: what each rank's launch computes (rows replicated on every rank -- decode rows
     # and short prefills -- count on each); flops_step: every global token once, the step's value
     flops_launch = float(sum(flops_r))
-    t_rank = [float(np.mean([events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)]))
-              for r in range(w.P)]
+    t_rank_all = [[events[k][r][0].elapsed_time(events[k][r][1]) for k in range(args.steps)] for r in range(w.P)]
+    t_rank = [float(np.mean(x)) for x in t_rank_all]
     t_merge = float(np.mean([events[k][w.P][0].elapsed_time(events[k][w.P][1]) for k in range(args.steps)]))
     t_insert = float(np.mean([events[k][w.P + 1][0].elapsed_time(events[k][w.P + 1][1]) for k in range(args.steps)]))
     avg_launch_ms = float(np.mean(t_rank))
@@ -353,6 +389,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": att_traffic},
         "attention": {"rank_ms": [round(x, 3) for x in t_rank],
+                      "rank_ms_min": [round(float(np.min(r_)), 3) for r_ in t_rank_all],
+                      "rank_ms_p90": [round(float(np.percentile(r_, 90)), 3) for r_ in t_rank_all],
                       "rank_tflops": [round(f / (t * 1e-3) / 1e12, 2) for f, t in zip(flops_r, t_rank)],
                       "balance_last_over_first": round(t_rank[-1] / t_rank[0], 4),
                       "tokens_per_s": round(w.T_glob / (ms_step * 1e-3), 1)},
@@ -387,6 +425,11 @@ def main():
                               "frac_hbm": round(sel_bytes / (t_sel * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                               "bytes": sel_bytes}
         out["config"]["topk_source"] = "selected on the GPU from hashed index scores"
+    if not args.no_box_reference:
+        ref = box_reference(dev)
+        ref["attention_frac_of_gemm"] = round(achieved / ref["gemm_bf16_tflops"], 4)
+        ref["merge_frac_of_copy"] = round(out["merge"]["GB/s"] / ref["copy_GB/s"], 4)
+        out["box_reference"] = ref
     if args.calib_copy:
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)

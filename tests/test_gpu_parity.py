@@ -173,6 +173,8 @@ EDGE = [
     (106, [600, 1], [700, 900], 2, 64, 512, 64),  # H = 64
     (108, [300, 1], [300, 500], 2, 128, 512, 64),  # H = 128 (the largest)
     (109, [200, 50, 7], [200, 90, 7], 3, 3, 512, 64),  # H = 3: row tiles mix tokens of a virtual row
+    (110, [1000, 16, 15], [1000, 16, 15], 8, 16, 512, 64),  # P = 8: 16 new tokens split, 15 replicated
+    (111, [300, 128, 127, 1], [300, 128, 127, 40], 64, 4, 64, 16),  # P = 64, the largest: 1-token chunks
 ]
 
 
@@ -621,6 +623,23 @@ def test_sparse_workspace_path(gpu_lib, seed):
         ref = hp.oracle_sparse(w, ws.plan, ws.q_bits, ws.lat_codes, ws.kv_scale, ws.rope_bits, ws.topk, ws.sink,
                                toks)
         check_merged(ws, ref, toks, SPARSE_O_TOL)
+
+
+def test_sparse_largest_window_and_topk(gpu_lib):
+    """The largest key sets the API takes, top-k 2048 and a 4096-key window, on a prefill where
+    early queries see the window cover their whole prefix (every selected index falls inside it
+    and counts once) and late ones see 2048 selected keys before a full window: the fp8 kernel
+    and the bf16 workspace path bit-identical, sampled tokens against the oracle, all finite."""
+    w = synth.custom(221, [7000], [7000], P=2, H=64, Dl=512, Dr=64, topk=2048, window=4096, kv_dtype="fp8",
+                     latent_std=1.0)
+    fp8 = SparseRun(w)
+    ws = SparseRun(w, workspace=True)
+    assert torch.equal(ws.bufs.o_cat.view(torch.int16), fp8.bufs.o_cat.view(torch.int16))
+    assert torch.equal(ws.bufs.lse_cat.view(torch.int32), fp8.bufs.lse_cat.view(torch.int32))
+    toks = hp.sample_tokens(w, fp8.plan, n_random=48)
+    print(f"[check] largest key sets: {len(toks)} sampled tokens", flush=True)
+    fp8.check_values(toks)
+    assert bool(torch.isfinite(fp8.bufs.o_cat.float()).all()) and bool(torch.isfinite(fp8.bufs.lse_cat).all())
 
 
 def test_sparse128k_p2_sampled(gpu_lib):

@@ -6,6 +6,8 @@ meet the same bounds as the packed path (max|O-O_ref| <= 1e-2, 3e-2 for fp8 late
 max|LSE-LSE_ref| <= 1e-3). A paged dense run is also bit-identical to the packed run of
 the same workload: paging changes addresses only.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -180,6 +182,26 @@ def test_paged_dense(gpu_lib, seed):
 
 # ------------------------------------------------------------------ fp8 quantise-on-insert
 
+
+def test_dense128k_p4_paged_sampled(gpu_lib):
+    """The 128K-token P=4 workload on a paged cache (a random table of 2048 64-row blocks, the
+    cache layout bench.py --paged times): every rank's partials bit-identical to the packed run
+    of the same inputs (itself checked against the oracle), sampled merged rows against the
+    oracle, every row finite."""
+    w = synth.workload(3)
+    paged = DenseCacheRun(w, seed=2024, paged=True)
+    packed = DenseCacheRun(w, paged=False)
+    assert torch.equal(paged.bufs.o_cat.view(torch.int16), packed.bufs.o_cat.view(torch.int16))
+    assert torch.equal(paged.bufs.lse_cat.view(torch.int32), packed.bufs.lse_cat.view(torch.int32))
+    del packed
+    toks = hp.sample_tokens(w, paged.plan, n_random=32)
+    print(f"[check] paged 128K: {len(toks)} sampled tokens", flush=True)
+    ref = hp.oracle_dense(w, paged.plan, paged.q_bits, paged.lat_bits, paged.rope_bits, paged.sink, toks)
+    o = on.bf16_to_f64(host_bits(paged.bufs.o))[toks]
+    hp.compare("paged 128K merged", o, paged.bufs.lse.cpu().numpy()[toks], np.stack([ref[g][2] for g in toks]),
+               np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
+    assert bool(torch.isfinite(paged.bufs.o.float()).all()) and bool(torch.isfinite(paged.bufs.lse).all())
+
 @pytest.mark.parametrize("dims", [(512, 64), (64, 16)])
 def test_fp8_insert_bit_exact(gpu_lib, dims):
     """Two insert calls on one cache: fresh blocks, a block opened by the first call and
@@ -347,6 +369,26 @@ def test_paged_sparse_workspace(gpu_lib, seed):
     assert torch.equal(ws.bufs.o_cat.view(torch.int16), fp8.bufs.o_cat.view(torch.int16))
     assert torch.equal(ws.bufs.lse_cat.view(torch.int32), fp8.bufs.lse_cat.view(torch.int32))
     ws.check_values()
+
+
+def test_sparse128k_p2_paged_quantised_sampled(gpu_lib):
+    """The 128K top-2048 workload in the layout bench.py --workload 4 --paged times: bf16 rows
+    quantised to fp8 on insert into a paged cache (a random table of 64-row blocks), dequantised
+    once into the bf16 workspace, sparse partials on it. Codes and block scales bit-exact against
+    the oracle's quantiser; sampled tokens (merged) against the oracle run on the oracle's own
+    codes; every row finite. The oracle's quantiser over all 131,072 rows takes 1-2 minutes of
+    host time."""
+    w = dataclasses.replace(synth.workload(4), kv_dtype="bf16")  # the fp8 workload's draws, kept in bf16
+    run = PagedSparseRun(w, 2024, workspace=True)
+    run.check_cache()
+    toks = hp.sample_tokens(w, run.plan, n_random=32)
+    print(f"[check] paged quantised 128K sparse: {len(toks)} sampled tokens", flush=True)
+    ref = hp.oracle_sparse(w, run.plan, run.q_bits, run.codes_o, run.scales_o, run.rope_bits, run.topk, run.sink,
+                           toks, rows_of=lambda b, keys: ok.paged_rows(run.bt, b, keys))
+    o = on.bf16_to_f64(host_bits(run.bufs.o))[toks]
+    hp.compare("paged quantised 128K sparse merged", o, run.bufs.lse.cpu().numpy()[toks],
+               np.stack([ref[g][2] for g in toks]), np.stack([ref[g][3] for g in toks]), SPARSE_O_TOL, LSE_TOL)
+    assert bool(torch.isfinite(run.bufs.o.float()).all()) and bool(torch.isfinite(run.bufs.lse).all())
 
 
 # ------------------------------------------------------------------ block ids outside the cache

@@ -552,6 +552,45 @@ def test_split_kv_dense(gpu_lib, seed):
     check_split_partials(run, sample, key_rows, O_TOL)
 
 
+def test_dense128k_p4_split_kv_sampled(gpu_lib):
+    """The 128K P=4 workload with each virtual row's keys cut into two ranges (the launch
+    bench.py --kv-splits 2 times): on sampled tokens, the merge of all eight (rank, split)
+    contributors against unsharded attention with the sink once, and for a subset both split
+    partials against the oracle restricted to each range's keys; every partial row finite."""
+    w = synth.workload(3)
+    S = 2
+    run = DenseRun(w, kv_splits=S)
+    toks = np.asarray(sorted(set(int(t) for t in hp.sample_tokens(w, run.plan, n_random=16))))
+    print(f"[check] split KV 128K: {len(toks)} sampled tokens", flush=True)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    sel_d = torch.from_numpy(toks).cuda()
+    hp.compare("128K merged over splits", on.bf16_to_f64(host_bits(run.bufs.o.index_select(0, sel_d))),
+               run.bufs.lse.index_select(0, sel_d).cpu().numpy(), np.stack([ref[g][2] for g in toks]),
+               np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
+    pos, req = hp.token_maps(run.plan)
+    sub = set(int(t) for t in toks[::4])
+    for r, rp in enumerate(run.plan.ranks):
+        vrow = np.searchsorted(rp.cu_seqlens_q, np.arange(rp.T_loc), side="right") - 1
+        for i in np.nonzero(np.isin(rp.local_gidx, list(sub)))[0]:
+            g = int(rp.local_gidx[i])
+            keys = np.arange(int(pos[g]) + 1)
+            base = int(w.kv_start[req[g]])
+            q = on.bf16_to_f64(run.q_bits[g])
+            for s_, (lo, hi) in enumerate(split_ranges(int(rp.vrow_kv_len[vrow[i]]), S)):
+                row = s_ * run.pl.T_total + run.plan.row_off[r] + int(i)
+                o_row = on.bf16_to_f64(host_bits(run.bufs.o_cat[row]))
+                lse_row = run.bufs.lse_cat[row].cpu().numpy()
+                k = keys[(keys >= lo) & (keys < hi)]
+                if len(k) == 0:
+                    assert np.all(o_row == 0) and np.all(np.isneginf(lse_row)), (g, s_)
+                    continue
+                o0, lse0, _, _ = oa.attend_keyset(q, on.bf16_to_f64(run.lat_bits[base + k]),
+                                                  on.bf16_to_f64(run.rope_bits[base + k]), float(w.scale))
+                hp.compare(f"token {g} rank {r} split {s_}", o_row[None], lse_row[None], o0[None], lse0[None],
+                           O_TOL, LSE_TOL)
+    assert bool(torch.isfinite(run.bufs.o_cat.float()).all())
+
+
 def test_split_kv_sparse(gpu_lib):
     """Split-KV on the sparse fp8 path: per-split partials and the merge over splits."""
     w = synth.custom(311, [900, 400], [900, 1300], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,

@@ -183,22 +183,24 @@ def test_paged_dense(gpu_lib, seed):
 # ------------------------------------------------------------------ fp8 quantise-on-insert
 
 
-def test_dense128k_p4_paged_sampled(gpu_lib):
-    """The 128K-token P=4 workload on a paged cache (a random table of 2048 64-row blocks, the
-    cache layout bench.py --paged times): every rank's partials bit-identical to the packed run
-    of the same inputs (itself checked against the oracle), sampled merged rows against the
-    oracle, every row finite."""
-    w = synth.workload(3)
+@pytest.mark.parametrize("cfg", [3, 5, 6])
+def test_dense_full_size_paged_sampled(gpu_lib, cfg):
+    """The full-size dense workloads on a paged cache (a random table of 64-row blocks, the cache
+    layout bench.py --paged times): 128K tokens at P=4, the mixed 8-prefill + 64-decode batch,
+    and the chunked-prefill step whose cached context sits in its blocks before the step. Every
+    rank's partials bit-identical to the packed run of the same inputs (itself checked against
+    the oracle), sampled merged rows against the oracle, every row finite."""
+    w = synth.workload(cfg)
     paged = DenseCacheRun(w, seed=2024, paged=True)
     packed = DenseCacheRun(w, paged=False)
     assert torch.equal(paged.bufs.o_cat.view(torch.int16), packed.bufs.o_cat.view(torch.int16))
     assert torch.equal(paged.bufs.lse_cat.view(torch.int32), packed.bufs.lse_cat.view(torch.int32))
     del packed
     toks = hp.sample_tokens(w, paged.plan, n_random=32)
-    print(f"[check] paged 128K: {len(toks)} sampled tokens", flush=True)
+    print(f"[check] paged workload {cfg}: {len(toks)} sampled tokens", flush=True)
     ref = hp.oracle_dense(w, paged.plan, paged.q_bits, paged.lat_bits, paged.rope_bits, paged.sink, toks)
     o = on.bf16_to_f64(host_bits(paged.bufs.o))[toks]
-    hp.compare("paged 128K merged", o, paged.bufs.lse.cpu().numpy()[toks], np.stack([ref[g][2] for g in toks]),
+    hp.compare(f"paged workload {cfg} merged", o, paged.bufs.lse.cpu().numpy()[toks], np.stack([ref[g][2] for g in toks]),
                np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
     assert bool(torch.isfinite(paged.bufs.o.float()).all()) and bool(torch.isfinite(paged.bufs.lse).all())
 

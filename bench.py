@@ -133,7 +133,8 @@ def cpu_baseline(w, n_tokens: int, seconds: float):
 
 def box_reference(dev):
     """Rates this box delivers outside the library, for context (timed after the step): a bf16
-    GEMM through torch.matmul (hipBLASLt), 8192^3, and a 1 GiB device-to-device copy."""
+    GEMM through torch.matmul (the BLAS library torch prefers on this device, recorded), 8192^3,
+    and a 1 GiB device-to-device copy."""
     import torch
     n = 8192
     g = torch.Generator(device=dev).manual_seed(0)
@@ -161,7 +162,12 @@ def box_reference(dev):
     t_copy = timed(lambda: dst.copy_(src), 10)
     nbytes = src.numel() * 2
     del src, dst
-    return {"gemm_bf16_tflops": round(2.0 * n ** 3 / (t_gemm * 1e-3) / 1e12, 1), "gemm": "torch.matmul bf16 8192^3",
+    try:
+        blas = str(torch.backends.cuda.preferred_blas_library()).split(".")[-1]
+    except Exception:  # older torch: not exposed
+        blas = "unknown"
+    return {"gemm_bf16_tflops": round(2.0 * n ** 3 / (t_gemm * 1e-3) / 1e12, 1),
+            "gemm": f"torch.matmul bf16 8192^3, preferred BLAS backend {blas}",
             "copy_GB/s": round(2.0 * nbytes / (t_copy * 1e-3) / 1e9, 1), "copy": "1 GiB device-to-device"}
 
 

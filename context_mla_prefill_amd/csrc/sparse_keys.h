@@ -113,12 +113,29 @@ __device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk,
     ks.pad_row = PAGED ? blk(0) * BN : 0;
     ks.n_sel_tiles = (topk + BN - 1) / BN;
     ks.n_tiles = ks.n_sel_tiles + (window + BN - 1) / BN;
-    for (int i = threadIdx.x; i < MAX_TOPK; i += NT) {
-        const int e = i < topk ? topk_idx[(int64_t)w.tok * topk + i] : -1;
-        const bool ok = e >= w.key_lo && e < w.key_hi && e <= w.p && (window == 0 || e < ks.win_lo);
-        int r = -1;
-        if (ok) r = PAGED ? blk(e >> 6) * BN + (e & (BN - 1)) : e;
-        sel[i] = r;
+    // Every thread's PER entries: all index loads issued before the first is used (and, paged,
+    // all block-table loads, at clamped columns so they need no branch), so the list costs one
+    // or two memory latencies instead of one per entry.
+    constexpr int PER = MAX_TOPK / NT;
+    static_assert(MAX_TOPK % NT == 0, "selected-row list split evenly over the threads");
+    int e[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = (int)threadIdx.x + j * NT;
+        e[j] = i < topk ? topk_idx[(int64_t)w.tok * topk + i] : -1;
+    }
+    int r[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if constexpr (PAGED)
+            r[j] = blk(max(e[j], 0) >> 6) * BN + (e[j] & (BN - 1));
+        else
+            r[j] = e[j];
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool ok = e[j] >= w.key_lo && e[j] < w.key_hi && e[j] <= w.p && (window == 0 || e[j] < ks.win_lo);
+        sel[(int)threadIdx.x + j * NT] = ok ? r[j] : -1;
     }
     if constexpr (PAGED) {
         const int nwb = window > 0 ? (w.p >> 6) - (ks.win_lo >> 6) + 1 : 0;  // <= MAX_WINDOW / BN + 1

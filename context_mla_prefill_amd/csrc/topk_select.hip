@@ -175,16 +175,35 @@ __global__ __launch_bounds__(NT, 6) void topk_select_kernel(const float* __restr
     uint32_t thr, need, equal;
     const bool whole = n <= CAND;
     if (whole) {
-        for (int64_t i = tid; i < n; i += NT) sh.key[i] = order_key(srow[i]);
+        // all of a thread's loads issued before any is used (one memory latency, not one per score)
+        constexpr int WPER = (CAND + NT - 1) / NT;
+        float x[WPER];
+#pragma unroll
+        for (int j = 0; j < WPER; ++j) {
+            const int64_t i = tid + (int64_t)j * NT;
+            x[j] = srow[min(i, n - 1)];  // n > k >= 1 here; past the row end re-reads its last score
+        }
+#pragma unroll
+        for (int j = 0; j < WPER; ++j) {
+            const int64_t i = tid + (int64_t)j * NT;
+            if (i < n) sh.key[i] = order_key(x[j]);
+        }
         __syncthreads();
         need = (uint32_t)k;
         thr = select_rank<true>([&](int64_t i) { return sh.key[i]; }, n, need, equal, sh);
     } else {
         // 1. threshold estimate: sample block b starts at floor(b * n / 32) rounded down to 4
-        for (int i = tid; i < NSAMP; i += NT) {
+        //    (all of a thread's sample loads issued before any is used)
+        static_assert(NSAMP % NT == 0, "sample split evenly over the threads");
+        float xs[NSAMP / NT];
+#pragma unroll
+        for (int j = 0; j < NSAMP / NT; ++j) {
+            const int i = tid + j * NT;
             const int64_t s0 = (((int64_t)(i >> 6) * n) >> 5) & ~(int64_t)3;
-            sh.key[i] = order_key(srow[s0 + (i & 63)]);
+            xs[j] = srow[s0 + (i & 63)];
         }
+#pragma unroll
+        for (int j = 0; j < NSAMP / NT; ++j) sh.key[tid + j * NT] = order_key(xs[j]);
         if (tid == 0) sh.count = 0;
         __syncthreads();
         uint32_t j = (uint32_t)min((int64_t)NSAMP, max((int64_t)1, (int64_t)(k + CAND) / 2 * NSAMP / n));

@@ -205,3 +205,115 @@ def test_fp8_dequant_rounding():
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert np.array_equal(got[ok], ref[ok])
+
+
+def _loop_attend(q_tok, lat_keys, rope_keys, scale, sink):
+    """Per-head explicit loops over an explicit key list (no matrix products)."""
+    H = q_tok.shape[0]
+    Dl = lat_keys.shape[1]
+    O = np.zeros((H, Dl))
+    L = np.zeros(H)
+    for h in range(H):
+        sc = [scale * (float(q_tok[h, :Dl] @ lat_keys[j]) + float(q_tok[h, Dl:] @ rope_keys[j]))
+              for j in range(len(lat_keys))]
+        den = sum(math.exp(x) for x in sc) + (0.0 if sink is None else math.exp(sink[h]))
+        O[h] = sum(math.exp(x) * lat_keys[j] for j, x in enumerate(sc)) / den
+        L[h] = math.log(den)
+    return O, L
+
+
+@pytest.mark.parametrize("block", [1, 3, 256])
+def test_attention_tokens_multi_request_batch(block):
+    """The oracle's batch driver on a packed batch of several requests: fresh prefills,
+    continuations (kv_len > q_len, context already cached), a short prefill and decode rows,
+    with KV segments at non-zero, gapped starts and the tokens asked in shuffled order.
+    Every token must equal its own request's causal prefix, attended alone: position
+    kv_len - q_len + i of request b attends packed rows kv_start[b] .. kv_start[b] + position
+    ("[Core] Add MRV2 virtual-batch PCP for MLA", "PCP algorithm": each request is handled on
+    its own; decode rows attend their whole context)."""
+    rng = np.random.default_rng(11)
+    H, Dl, Dr = 3, 8, 4
+    q_lens = np.array([13, 5, 1, 2, 1, 7])
+    kv_lens = np.array([13, 20, 9, 2, 1, 30])
+    kv_start = np.array([4, 40, 17, 70, 0, 80])  # gapped and out of batch order
+    n_kv = int((kv_start + kv_lens).max()) + 3
+    lat, rope = _rand(rng, n_kv, Dl), _rand(rng, n_kv, Dr)
+    T = int(q_lens.sum())
+    q = _rand(rng, T, H, Dl + Dr)
+    sink = np.array([0.5, -1.0, 2.0])
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    req = np.repeat(np.arange(len(q_lens)), q_lens)
+    pos = np.concatenate([np.arange(k - n, k) for n, k in zip(q_lens, kv_lens)])
+    tokens = rng.permutation(T)
+    out = oa.attention_tokens(tokens, q_of=lambda ts: q[ts], pos_of=lambda ts: pos[ts],
+                              req_of=lambda ts: req[ts], kv_start=kv_start,
+                              lat_rows=lambda a, b: lat[a:b], rope_rows=lambda a, b: rope[a:b],
+                              scale=0.3, sink=sink, block=block)
+    assert sorted(out) == list(range(T))
+    for t in range(T):
+        b, p = int(req[t]), int(pos[t])
+        assert cu[b] <= t < cu[b + 1]
+        rows = kv_start[b] + np.arange(p + 1)
+        o0, l0, o, l = out[t]
+        ko0, kl0, ko, kl = oa.attend_keyset(q[t], lat[rows], rope[rows], 0.3, sink)
+        np.testing.assert_allclose(o0, ko0, atol=1e-12)
+        np.testing.assert_allclose(l0, kl0, atol=1e-12)
+        np.testing.assert_allclose(o, ko, atol=1e-12)
+        np.testing.assert_allclose(l, kl, atol=1e-12)
+        # and against explicit loops over the same key rows
+        bo, bl = _loop_attend(q[t], lat[rows], rope[rows], 0.3, sink)
+        np.testing.assert_allclose(o, bo, atol=1e-12)
+        np.testing.assert_allclose(l, bl, atol=1e-12)
+        bo0, bl0 = _loop_attend(q[t], lat[rows], rope[rows], 0.3, None)
+        np.testing.assert_allclose(o0, bo0, atol=1e-12)
+        np.testing.assert_allclose(l0, bl0, atol=1e-12)
+
+
+def test_attention_tokens_subset_and_isolation():
+    """Asking for a subset gives the same rows as asking for all of them, and a request's
+    rows do not change when another request's KV changes (request isolation)."""
+    rng = np.random.default_rng(12)
+    H, Dl, Dr = 2, 8, 4
+    q_lens, kv_lens, kv_start = np.array([6, 4]), np.array([6, 9]), np.array([0, 6])
+    lat, rope = _rand(rng, 15, Dl), _rand(rng, 15, Dr)
+    q = _rand(rng, 10, H, Dl + Dr)
+    req = np.repeat([0, 1], q_lens)
+    pos = np.concatenate([np.arange(6), np.arange(5, 9)])
+
+    def run(lat_, toks):
+        return oa.attention_tokens(toks, q_of=lambda ts: q[ts], pos_of=lambda ts: pos[ts],
+                                   req_of=lambda ts: req[ts], kv_start=kv_start,
+                                   lat_rows=lambda a, b: lat_[a:b], rope_rows=lambda a, b: rope[a:b],
+                                   scale=0.4)
+
+    full = run(lat, np.arange(10))
+    part = run(lat, np.array([9, 2, 6]))
+    for t in (9, 2, 6):
+        for a, b in zip(full[t], part[t]):
+            np.testing.assert_array_equal(a, b)
+    lat2 = lat.copy()
+    lat2[6:] += 1.0  # request 1's KV only
+    other = run(lat2, np.arange(6))
+    for t in range(6):
+        for a, b in zip(full[t], other[t]):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_sparse_keyset_drops_indices_past_the_query():
+    """Selected indices after the query's position are not in its causal prefix and act as
+    pads, as do negative ones; duplicates and window members count once."""
+    p, W = 10, 4
+    sel = np.array([3, 8, 11, 15, -1, 3, 10, 0, -7, 10 ** 6, 9])
+    assert list(oa.sparse_keyset(p, sel, W)) == [0, 3, 7, 8, 9, 10]
+    # every index past p at p = 0 leaves the window alone
+    assert list(oa.sparse_keyset(0, np.array([1, 2, 5]), W)) == [0]
+    # no window: only the selected prefix keys, deduplicated
+    assert list(oa.sparse_keyset(p, sel, 0)) == [0, 3, 8, 9, 10]
+    # brute-force membership on random rows
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        p = int(rng.integers(0, 50))
+        W = int(rng.integers(0, 20))
+        sel = rng.integers(-3, 70, size=int(rng.integers(0, 30)))
+        want = sorted({int(x) for x in sel if 0 <= x <= p} | {j for j in range(p + 1) if j > p - W})
+        assert list(oa.sparse_keyset(p, sel, W)) == want

@@ -105,6 +105,22 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _need(t, nbytes: int, what: str):
+    """A tensor / array handed to the library must hold at least the bytes the call will
+    touch (the C ABI takes bare pointers and cannot check this itself)."""
+    if t is None or nbytes <= 0:
+        return
+    if isinstance(t, np.ndarray):
+        have = t.nbytes
+    elif hasattr(t, "untyped_storage"):  # bytes from the first element to the end of the storage
+        st = t.untyped_storage()
+        have = st.nbytes() - (t.data_ptr() - st.data_ptr())
+    else:  # a bare address: its size is the caller's to guarantee
+        return
+    if have < nbytes:
+        raise MlaError(MLA_ERR_INVALID_ARG, f"{what}: holds {have} bytes, the call reads or writes {nbytes}")
+
+
 def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -143,6 +159,12 @@ def pcp_partition(q_lens, kv_lens, kv_start, P, T_glob, n_vrows, T_loc_total, cu
 
 def pcp_kv_insert(local_latent, local_rope, slot, T_loc, D_latent, D_rope, kv_dtype, N_kv, kv_latent,
                   kv_rope, stream=None):
+    eb = 2 if kv_dtype == MLA_KV_BF16 else 1
+    _need(local_latent, T_loc * D_latent * eb, "pcp_kv_insert local_latent")
+    _need(local_rope, T_loc * D_rope * 2, "pcp_kv_insert local_rope")
+    _need(slot, T_loc * 4, "pcp_kv_insert slot")
+    _need(kv_latent, N_kv * D_latent * eb, "pcp_kv_insert kv_latent")
+    _need(kv_rope, N_kv * D_rope * 2, "pcp_kv_insert kv_rope")
     st = load().pcp_kv_insert(_ptr(local_latent), _ptr(local_rope), _ptr(slot), T_loc, D_latent, D_rope,
                               kv_dtype, N_kv, _ptr(kv_latent), _ptr(kv_rope), _stream(stream))
     _check(st, "pcp_kv_insert")
@@ -150,18 +172,30 @@ def pcp_kv_insert(local_latent, local_rope, slot, T_loc, D_latent, D_rope, kv_dt
 
 def pcp_kv_insert_fp8(local_latent, local_rope, slot, T, D_latent, D_rope, N_kv, kv_latent, kv_rope, kv_scale,
                       stream=None):
+    _need(local_latent, T * D_latent * 2, "pcp_kv_insert_fp8 local_latent (bf16 rows)")
+    _need(local_rope, T * D_rope * 2, "pcp_kv_insert_fp8 local_rope")
+    _need(slot, T * 4, "pcp_kv_insert_fp8 slot")
+    _need(kv_latent, N_kv * D_latent, "pcp_kv_insert_fp8 kv_latent")
+    _need(kv_rope, N_kv * D_rope * 2, "pcp_kv_insert_fp8 kv_rope")
+    _need(kv_scale, (N_kv + 63) // 64 * 4, "pcp_kv_insert_fp8 kv_scale")
     st = load().pcp_kv_insert_fp8(_ptr(local_latent), _ptr(local_rope), _ptr(slot), T, D_latent, D_rope, N_kv,
                                   _ptr(kv_latent), _ptr(kv_rope), _ptr(kv_scale), _stream(stream))
     _check(st, "pcp_kv_insert_fp8")
 
 
 def pcp_kv_dequant_fp8(kv_latent, kv_scale, N_kv, D_latent, blocks, n_blocks, ws, stream=None):
+    _need(kv_latent, N_kv * D_latent, "pcp_kv_dequant_fp8 kv_latent")
+    _need(kv_scale, (N_kv + 63) // 64 * 4, "pcp_kv_dequant_fp8 kv_scale")
+    _need(blocks, n_blocks * 4, "pcp_kv_dequant_fp8 blocks")
+    _need(ws, N_kv * D_latent * 2, "pcp_kv_dequant_fp8 ws")
     st = load().pcp_kv_dequant_fp8(_ptr(kv_latent), _ptr(kv_scale), N_kv, D_latent, _ptr(blocks), n_blocks, _ptr(ws),
                                    _stream(stream))
     _check(st, "pcp_kv_dequant_fp8")
 
 
 def sparse_topk_select(scores, ld, positions, T, k, topk_idx, stream=None):
+    _need(positions, T * 4, "sparse_topk_select positions")
+    _need(topk_idx, T * k * 4, "sparse_topk_select topk_idx")
     st = load().sparse_topk_select(_ptr(scores), ld, _ptr(positions), T, k, _ptr(topk_idx), _stream(stream))
     _check(st, "sparse_topk_select")
 
@@ -170,6 +204,19 @@ def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positio
                       D_latent, D_rope, scale, o_partial, lse, N_kv, kv_dtype=MLA_KV_BF16, kv_scale=None,
                       topk_idx=None, topk=0, window=0, kv_splits=1, split_stride=0,
                       vrow_kv_len=None, block_table=None, bt_stride=0, vrow_req=None) -> mla_partial_args:
+    rows = (split_stride * (kv_splits - 1) + T_loc) if kv_splits > 1 else T_loc
+    eb = 2 if kv_dtype == MLA_KV_BF16 else 1
+    _need(q, T_loc * H * (D_latent + D_rope) * 2, "mla_prefill_partial q")
+    _need(latent_kv, N_kv * D_latent * eb, "mla_prefill_partial latent_kv")
+    _need(rope_k, N_kv * D_rope * 2, "mla_prefill_partial rope_k")
+    _need(positions, T_loc * 4, "mla_prefill_partial positions")
+    _need(topk_idx, T_loc * topk * 4, "mla_prefill_partial topk_idx")
+    _need(o_partial, rows * H * D_latent * 2, "mla_prefill_partial o_partial")
+    _need(lse, rows * H * 4, "mla_prefill_partial lse")
+    _need(cu_seqlens_q, (n_vrows + 1) * 4, "mla_prefill_partial cu_seqlens_q")
+    _need(vrow_kv_start, n_vrows * 4, "mla_prefill_partial vrow_kv_start")
+    if kv_dtype != MLA_KV_BF16:
+        _need(kv_scale, (N_kv + 63) // 64 * 4, "mla_prefill_partial kv_scale")
     return mla_partial_args(
         q=_ptr(q), latent_kv=_ptr(latent_kv), kv_scale=_ptr(kv_scale), rope_k=_ptr(rope_k),
         cu_seqlens_q=_ptr(cu_seqlens_q), vrow_kv_start=_ptr(vrow_kv_start), positions=_ptr(positions),
@@ -187,6 +234,12 @@ def mla_prefill_partial(args: mla_partial_args, stream=None):
 
 def pcp_lse_merge(o_cat, lse_cat, merge_src, P, T_glob, H, D_v, R_total, sink, o_out, lse_out,
                   stream=None, kv_splits=1, split_stride=0):
+    _need(o_cat, R_total * H * D_v * 2, "pcp_lse_merge o_cat")
+    _need(lse_cat, R_total * H * 4, "pcp_lse_merge lse_cat")
+    _need(merge_src, T_glob * P * 4, "pcp_lse_merge merge_src")
+    _need(o_out, T_glob * H * D_v * 2, "pcp_lse_merge o_out")
+    _need(lse_out, T_glob * H * 4, "pcp_lse_merge lse_out")
+    _need(sink, H * 4, "pcp_lse_merge sink")
     st = load().pcp_lse_merge(_ptr(o_cat), _ptr(lse_cat), _ptr(merge_src), P, T_glob, H, D_v, R_total,
                               kv_splits, split_stride, _ptr(sink), _ptr(o_out), _ptr(lse_out), _stream(stream))
     _check(st, "pcp_lse_merge")

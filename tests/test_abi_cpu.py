@@ -214,3 +214,25 @@ def test_merge_rejects_too_many_heads():
     f = _P(FAKE)
     st, _ = _status(lambda: _lib.pcp_lse_merge(f, f, f, 2, 4, 129, 64, 8, None, f, None, stream=0))
     assert st == _lib.MLA_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_buffers_smaller_than_the_call():
+    """The binding checks each tensor's bytes (to the end of its storage, so views into a
+    larger buffer pass) against what the call reads or writes, before the library runs: fp8
+    codes (one byte per element) handed to the fp8 insert, which reads bf16 rows, are refused."""
+    import torch
+    T, Dl, Dr, N = 8, 512, 64, 64
+    codes = torch.zeros(T, Dl, dtype=torch.uint8)
+    rope = torch.zeros(T, Dr, dtype=torch.bfloat16)
+    slot = torch.zeros(T, dtype=torch.int32)
+    kv = torch.zeros(N, Dl, dtype=torch.uint8)
+    kv_rope = torch.zeros(N, Dr, dtype=torch.bfloat16)
+    scale = torch.zeros(1, dtype=torch.float32)
+    with pytest.raises(_lib.MlaError, match="local_latent"):
+        _lib.pcp_kv_insert_fp8(codes, rope, slot, T, Dl, Dr, N, kv, kv_rope, scale, stream=0)
+    # a view: its storage runs past the view, which is what a kernel writing later split
+    # slices through the view's pointer relies on
+    big = torch.zeros(4 * T, 16, Dl, dtype=torch.bfloat16)
+    _lib._need(big[T:2 * T], 3 * T * 16 * Dl * 2, "view")
+    with pytest.raises(_lib.MlaError):
+        _lib._need(big[T:2 * T], 3 * T * 16 * Dl * 2 + 2, "view")

@@ -13,6 +13,8 @@ import pytest
 import torch
 
 import helpers as hp
+from paged_tables import corrupt_table, make_block_table, rank_order, request_rows
+import paged_tables as pt
 from context_mla_prefill_amd import _lib, synth
 from context_mla_prefill_amd import pipeline as pp
 from oracle import kvcache as ok
@@ -30,26 +32,6 @@ def dev_bf16(bits):
 
 def host_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def make_block_table(w, seed, spare=5, pad=2):
-    """Each request's ceil(kv_len / 64) blocks drawn without replacement from a pool with
-    spare blocks, in random order; pad columns hold -1 and are never read."""
-    rng = np.random.default_rng(seed)
-    nb = (w.kv_lens.astype(np.int64) + 63) // 64
-    n_blocks = int(nb.sum()) + spare
-    perm = rng.permutation(n_blocks)
-    bt = np.full((w.n_req, int(nb.max(initial=0)) + pad), -1, np.int32)
-    k = 0
-    for b in range(w.n_req):
-        bt[b, :nb[b]] = perm[k:k + nb[b]]
-        k += int(nb[b])
-    return bt, n_blocks
-
-
-def rank_order(plan):
-    """Global tokens in rank-concatenated row order."""
-    return np.concatenate([rp.local_gidx for rp in plan.ranks]).astype(np.int64)
 
 
 def context_rows(w):
@@ -196,7 +178,7 @@ def test_dense_full_size_paged_sampled(gpu_lib, cfg):
     assert torch.equal(paged.bufs.o_cat.view(torch.int16), packed.bufs.o_cat.view(torch.int16))
     assert torch.equal(paged.bufs.lse_cat.view(torch.int32), packed.bufs.lse_cat.view(torch.int32))
     del packed
-    toks = hp.sample_tokens(w, paged.plan, n_random=32)
+    toks = hp.sample_tokens(w, paged.plan)
     print(f"[check] paged workload {cfg}: {len(toks)} sampled tokens", flush=True)
     ref = hp.oracle_dense(w, paged.plan, paged.q_bits, paged.lat_bits, paged.rope_bits, paged.sink, toks)
     o = on.bf16_to_f64(host_bits(paged.bufs.o))[toks]
@@ -260,6 +242,9 @@ class PagedSparseRun:
         self.w, self.kv_splits = w, kv_splits
         self.plan = plan = hp.oracle_plan(w)
         print(f"[run] sparse paged {w.name} T={w.T_glob} kv_splits={kv_splits}", flush=True)
+        # the library quantises bf16 rows on insert: a workload drawn as fp8 codes would hand
+        # the insert one byte per element where it reads two
+        assert w.kv_dtype == "bf16", "PagedSparseRun inserts bf16 latent rows"
         self.q_bits, self.lat_bits, self.rope_bits = synth.q_rows(w), synth.latent_rows(w), synth.rope_rows(w)
         self.topk = synth.topk_rows(w)
         self.sink = synth.sink(w)
@@ -383,7 +368,7 @@ def test_sparse128k_p2_paged_quantised_sampled(gpu_lib):
     w = dataclasses.replace(synth.workload(4), kv_dtype="bf16")  # the fp8 workload's draws, kept in bf16
     run = PagedSparseRun(w, 2024, workspace=True)
     run.check_cache()
-    toks = hp.sample_tokens(w, run.plan, n_random=32)
+    toks = hp.sample_tokens(w, run.plan)
     print(f"[check] paged quantised 128K sparse: {len(toks)} sampled tokens", flush=True)
     ref = hp.oracle_sparse(w, run.plan, run.q_bits, run.codes_o, run.scales_o, run.rope_bits, run.topk, run.sink,
                            toks, rows_of=lambda b, keys: ok.paged_rows(run.bt, b, keys))
@@ -395,39 +380,22 @@ def test_sparse128k_p2_paged_quantised_sampled(gpu_lib):
 
 # ------------------------------------------------------------------ block ids outside the cache
 
-def corrupt_table(bt, n_blocks, b):
-    """Request b's first three block-table entries replaced by ids outside the cache: past its
-    end, negative, and 2^24 (its rows, 2^30 and up, still fit int32)."""
-    bad = bt.copy()
-    bad[b, :3] = [n_blocks + 5, -3, 1 << 24]
-    return bad
-
-
-def request_rows(plan, lo, hi):
-    """Rank-concatenated rows of the global tokens [lo, hi)."""
-    g = rank_order(plan)
-    return np.nonzero((g >= lo) & (g < hi))[0]
-
-
-@pytest.mark.skip(reason="faulted the GPU (an illegal memory access reported after the dense run on the "
-                         "table with block ids outside the cache); the cause is not yet shown on the CPU, so the "
-                         "case stays off the GPU")
 def test_paged_block_ids_outside_the_cache(gpu_lib):
-    """Block-table entries outside the cache break a stated precondition: they give wrong values
-    for the keys they map, never an access outside the cache (the dense kernel clamps block ids
-    into the cache as it loads them; the sparse kernels read through whole-cache buffer views;
-    the inserts skip slots outside the cache). Request 1's table holds such entries; request 0's
+    """Block-table entries outside the cache give wrong values for the keys they map, never an
+    access outside the cache: the dense kernel clamps block ids into the cache as it loads them,
+    the sparse kernels clamp every key row into the cache before forming an offset, and the
+    inserts skip slots outside the cache (every access of this test is modelled on the CPU in
+    test_paged_access_model.py). Request 1's table holds such entries; request 0's
     partials equal those of the run with the valid table bit for bit, on the dense path and on
     the sparse path (bf16 workspace and fp8 in the kernel)."""
-    wd = synth.custom(404, [600, 400], [600, 400], P=2, H=16, Dl=512, Dr=64)
+    wd = synth.custom(**pt.OUT_OF_CACHE_DENSE)
     bt, nb = make_block_table(wd, 404)
     rows = torch.from_numpy(request_rows(hp.oracle_plan(wd), 0, 600)).cuda()
     good = DenseCacheRun(wd, table=(bt, nb))
     bad = DenseCacheRun(wd, table=(corrupt_table(bt, nb, 1), nb))
     assert torch.equal(good.bufs.o_cat[rows].view(torch.int16), bad.bufs.o_cat[rows].view(torch.int16))
     assert torch.equal(good.bufs.lse_cat[rows].view(torch.int32), bad.bufs.lse_cat[rows].view(torch.int32))
-    ws = synth.custom(504, [700, 500], [700, 500], P=2, H=64, Dl=512, Dr=64, topk=128, window=64,
-                      kv_dtype="fp8", latent_std=1.0)
+    ws = synth.custom(**pt.OUT_OF_CACHE_SPARSE)
     bt, nb = make_block_table(ws, 504)
     rows = torch.from_numpy(request_rows(hp.oracle_plan(ws), 0, 700)).cuda()
     for workspace in (True, False):

@@ -279,8 +279,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     // read by v_readlane; the next 64 are fetched one tile before they are needed.
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[v] * bt_stride : nullptr;
     const int nblk = (int)(last >> 6) + 1;
-    // Block ids outside the cache are clamped into it as the window loads (wrong values, never
-    // a stray access); the cache holds whole blocks, so every tile -- one block, or the last key
+    // Block ids outside the cache are clamped into it as the window loads (the keys they map read
+    // wrong rows of the cache, never memory outside it); the cache holds whole blocks, so every tile -- one block, or the last key
     // alone -- stays inside it.
     const int blk_max = (int)(N_kv >> 6) - 1;
     int bw_base = 0, bw_v = 0;

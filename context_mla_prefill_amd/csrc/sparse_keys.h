@@ -99,8 +99,8 @@ __device__ __forceinline__ SparseKeys<PAGED> sparse_keys(int* sel, int* win_blk,
                                                          int topk, int window, const SparseWork& w,
                                                          const int32_t* __restrict__ bt_row, int bt_stride) {
     // paged: table columns past bt_stride read its last entry; the kernels clamp every row
-    // into the cache before they form an offset from it (a block id outside the cache gives
-    // wrong values, never a stray access)
+    // into the cache before they form an offset from it (a block id outside the cache reads
+    // wrong rows of the cache, never memory outside it)
     auto blk = [&](int col) { return bt_row[min(col, bt_stride - 1)]; };
     SparseKeys<PAGED> ks;
     ks.sel = sel;

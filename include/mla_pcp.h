@@ -19,10 +19,10 @@
  *    mla_pcp_last_error() describes the problem. No call aborts or throws.
  *  - Kernels bound their memory accesses by the sizes passed in. The device index arrays
  *    one call passes to the next (cu_seqlens, vrow_* arrays, positions, local_gidx,
- *    merge_src as pcp_partition writes them) must be consistent with those sizes, and every
- *    block-table entry a request uses must name a block of the cache; within that, device
- *    data that breaks a stated precondition (selected indices out of range, slots outside
- *    [0, N_kv), NaN scores) gives wrong values, never an out-of-bounds access.
+ *    merge_src as pcp_partition writes them) must be consistent with those sizes; within
+ *    that, device data that breaks a stated precondition (selected indices out of range,
+ *    slots outside [0, N_kv), block-table entries that name no block of the cache, NaN
+ *    scores) gives wrong values, never an out-of-bounds access.
  */
 #ifndef MLA_PCP_H
 #define MLA_PCP_H

@@ -18,12 +18,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_pcp.so")
 
-SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense.hip", "attn_sparse.hip",
+SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense.hip", "attn_dense_wide.hip",
+           "attn_sparse.hip",
            "attn_sparse_bf16.hip", "topk_select.hip"]
 
 # Per-file flags. The attention kernels keep O and the scores in VGPRs (MFMA VGPR form)
 # so its rare rescale is plain VALU work, leaving the AGPRs to Q.
 EXTRA = {"attn_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attn_dense_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_sparse_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

@@ -534,6 +534,7 @@ hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream) {
+    if (a.D_latent == 512) return launch_dense_wide_partial(a, stream);  // 128-row workgroups
     if (a.block_table) {
         if (a.D_latent == 512) return launch_dense<512, 64, true>(a, stream);
         return launch_dense<64, 16, true>(a, stream);

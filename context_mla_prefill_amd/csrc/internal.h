@@ -42,6 +42,7 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* po
                               int32_t* topk_idx, hipStream_t stream);
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream);
+hipError_t launch_dense_wide_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_sparse_bf16_partial(const mla_partial_args& a, hipStream_t stream);
 

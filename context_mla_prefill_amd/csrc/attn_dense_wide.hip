@@ -168,24 +168,26 @@ __device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& v, const bf16x8
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
 }
 
+// Masks the scores of keys past this lane's row position: score s[i] is tile key
+// 16 (i / 8) + 4 (i % 4) + 2 ((i / 4) % 2) + half, visible when <= rel_h + half (the row's
+// position minus the tile's first key; a negative value masks the whole tile).
+__device__ __forceinline__ void causal_mask(f32x16& s, int rel_h) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int off = 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1);
+        s[i] = off <= rel_h ? s[i] : -INFINITY;
+    }
+}
+
 // Softmax of one tile for this lane's row, split into pieces that interleave with the 32 P V
-// MFMAs of the previous tile: pieces 0-8 the causal mask, the row max, the reference (set by the first tile
+// MFMAs of the previous tile: pieces 0-8 the row max, the reference (set by the first tile
 // with a visible key) and whether the max passed the reference's slack; 9-24 the
 // probabilities against the reference (rounded to bf16) and their sum.
 struct Softmax {
     float a[8], mloc, mn, mu, x[16], l;
     bool over;
-    // s is masked in place by pieces 0-3 (4 scores each): score i is tile key
-    // 16 (i / 8) + 4 (i % 4) + 2 ((i / 4) % 2) + half, visible when <= rel (the row's position
-    // minus the tile's first key; -1 masks the whole tile).
-    __device__ __forceinline__ void piece(int k, f32x16& s, int rel_h, float m_ref, float scale_log2,
-                                          bf16x8 (&pk)[2]) {
+    __device__ __forceinline__ void piece(int k, const f32x16& s, float m_ref, float scale_log2, bf16x8 (&pk)[2]) {
         if (k < 4) {
-#pragma unroll
-            for (int i = 4 * k; i < 4 * k + 4; ++i) {
-                const int off = 16 * (i >> 3) + 4 * (i & 3) + 2 * ((i >> 2) & 1);
-                s[i] = off <= rel_h ? s[i] : -INFINITY;
-            }
             a[2 * k] = fmaxf(s[4 * k], s[4 * k + 1]);
             a[2 * k + 1] = fmaxf(s[4 * k + 2], s[4 * k + 3]);
         } else if (k == 4) {
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
     // P V of the previous tile (kvp, probabilities pp) beside the softmax of this tile's scores
     // s: 32 MFMAs (16 column blocks x two 16-key halves), V^T reads PV_AHEAD_W MFMAs ahead, and
     // one piece of the softmax per MFMA, each chunk fenced so the interleave holds.
-    auto pv_softmax = [&](const char* kvp, const LaneOffs& lo, bf16x8 (&pp)[2], f32x16& s, int rel_h, Softmax& sm,
+    auto pv_softmax = [&](const char* kvp, const LaneOffs& lo, bf16x8 (&pp)[2], const f32x16& s, Softmax& sm,
                           bf16x8 (&pn)[2], auto do_pv, auto do_soft) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, SOFT = decltype(do_soft)::value;
         constexpr int NM = 2 * NBO;
@@ -417,15 +419,15 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
                 if (m + PV_AHEAD_W < NM) vread(m + PV_AHEAD_W);
                 pv_mfma(acc_o[m % NBO], vv[m % NVB], pp[m / NBO]);
             }
-            if constexpr (SOFT) sm.piece(m, s, rel_h, m_ref, scale_log2, pn);
+            if constexpr (SOFT) sm.piece(m, s, m_ref, scale_log2, pn);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // One tile step: wait for tile kt (buffer cur), issue tile kt+1 into nxt, Q K^T on cur;
     // then P V of tile kt-1 (buffer prv, probabilities pprev) beside this tile's softmax. The
-    // causal mask is applied branch-free (the step has no internal control flow, so O keeps one
-    // home in AGPRs); a tile past the row's last one (kt >= n_tiles) is masked whole.
+    // step's only branch (the causal mask) touches the scores alone, so O keeps one home in
+    // AGPRs; a tile past the row's last one (kt >= n_tiles) is masked whole.
     bf16x8 pprev[2];
     auto step = [&](const char* cur, const char* prv, char* nxt, int kt, auto has_prev) __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
@@ -433,10 +435,12 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         const TileSrc src(lat, rope, tile_rows(kt + 1));  // clamped past the last tile
         const LaneOffs lo = lane_offs();
         f32x16 s = qk_tile(cur, lo, src, nxt);
-        const int rel_h = (kt < n_tiles ? pos - kt * TK : -1) - half;
+        // wave-uniform: a causal diagonal crosses this tile, or it is past the last one (the
+        // branch touches only the scores, never O)
+        if (kt * TK + TK - 1 > pmin || kt >= n_tiles) causal_mask(s, (kt < n_tiles ? pos - kt * TK : -1) - half);
         Softmax sm;
         bf16x8 pn[2];
-        pv_softmax(prv, lo, pprev, s, rel_h, sm, pn, has_prev, std::true_type{});
+        pv_softmax(prv, lo, pprev, s, sm, pn, has_prev, std::true_type{});
         m_ref = sm.mn;
         m_true = fmaxf(m_true, sm.mloc);
         over = over || sm.over;
@@ -449,8 +453,8 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         const LaneOffs lo = lane_offs();
         Softmax sm;
         bf16x8 pn[2];
-        f32x16 s{};
-        pv_softmax(kvp, lo, pprev, s, 0, sm, pn, std::true_type{}, std::false_type{});
+        const f32x16 s{};
+        pv_softmax(kvp, lo, pprev, s, sm, pn, std::true_type{}, std::false_type{});
     };
 
     // Pass 0 against first-tile references; pass 1 only if some row of the workgroup passed

@@ -253,12 +253,9 @@ def main():
         # every key of every request in its block before the step (context rows stay, the step
         # re-inserts the new ones)
         n_cache = int(nb.sum()) * 64
-        bt_d = torch.from_numpy(block_table).to(dev).long()
-        reqs = torch.repeat_interleave(torch.arange(w.n_req, device=dev), torch.from_numpy(w.kv_lens).to(dev).long())
-        starts = torch.from_numpy(np.concatenate([[0], np.cumsum(w.kv_lens.astype(np.int64))[:-1]])).to(dev)
-        pos = torch.arange(w.N_kv, device=dev) - starts[reqs]
-        dst = bt_d[reqs, pos // 64] * 64 + pos % 64
-        src = torch.from_numpy(w.kv_start).to(dev).long()[reqs] + pos
+        # every key's cache row and its packed source row, both from the library's slot map
+        dst = pp.cache_rows(w.kv_lens, w.kv_lens, w.kv_start, block_table=block_table, device=dev)
+        src = pp.cache_rows(w.kv_lens, w.kv_lens, w.kv_start, device=dev)
         kv_rope = torch.empty(n_cache, w.Dr, dtype=torch.bfloat16, device=dev)
         kv_rope[dst] = rope_full[src]
         if quantise:
@@ -271,7 +268,7 @@ def main():
         else:
             kv_lat = torch.empty(n_cache, w.Dl, dtype=torch.bfloat16, device=dev)
             kv_lat[dst] = lat_full[src]
-        del bt_d, reqs, starts, pos, dst, src
+        del dst, src
     else:
         kv_lat = lat_full.clone()  # context rows present before the step; new rows are re-inserted
         kv_rope = rope_full.clone()
@@ -408,13 +405,17 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if sparse:
-        # algorithmic gather: every key of a query's set once per 64-head workgroup: a bf16
-        # workspace row + bf16 rope row, or an fp8 row + bf16 rope row + its fp32 scale
-        per_key = 2 * w.Dl + 2 * w.Dr if use_ws else w.Dl + 2 * w.Dr + 4
-        gbytes_r = [float(n_keys[g].sum()) * (w.H // 64) * per_key for g in gidx_r]
-        gbs = float(np.mean([b / (t * 1e-3) / 1e9 for b, t in zip(gbytes_r, t_rank)]))
-        out["gather"] = {"bytes_per_rank": [round(b) for b in gbytes_r], "GB/s": round(gbs, 1),
-                         "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        # algorithmic gather: every key of a query's set once per 64-head workgroup, as the
+        # method stores it: the fp8 latent row, the bf16 rope row and the row's fp32 scale. The
+        # workspace path reads a bf16 latent row instead (its own bytes, reported beside).
+        alg_key = w.Dl + 2 * w.Dr + 4
+        path_key = 2 * w.Dl + 2 * w.Dr if use_ws else alg_key
+        keys_r = [float(n_keys[g].sum()) * (w.H // 64) for g in gidx_r]
+        gbs = float(np.mean([k * alg_key / (t * 1e-3) / 1e9 for k, t in zip(keys_r, t_rank)]))
+        pbs = float(np.mean([k * path_key / (t * 1e-3) / 1e9 for k, t in zip(keys_r, t_rank)]))
+        out["gather"] = {"bytes_per_key": alg_key, "bytes_per_rank": [round(k * alg_key) for k in keys_r],
+                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                         "path_bytes_per_key": path_key, "path_GB/s": round(pbs, 1)}
     if use_ws:
         t_dq = float(np.mean([events[k][w.P + 3][0].elapsed_time(events[k][w.P + 3][1]) for k in range(args.steps)]))
         dq_bytes = float(n_cache) * (w.Dl + 2 * w.Dl) + (n_cache + 63) // 64 * 4

@@ -357,9 +357,28 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         return o;
     };
 
+    // V^T operands of the P V MFMAs, PV_AHEAD_W MFMAs ahead: MFMA m (16 column blocks x two
+    // 16-key halves) reads two transposing 4-key slices of column block m % 16.
+    constexpr int NVB = PV_AHEAD_W + 1;
+    struct VOps {
+        bf16x8 v[NVB];
+    };
+    auto vread = [&](VOps& vo, const char* kvp, const LaneOffs& lo, int m) __attribute__((always_inline)) {
+        const int h = m / NBO, d = m % NBO;
+        const char* vb = kvp + lo.v;
+        const int o0 = 16 * h * LAT_STRIDE + d * 64;
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o0));
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + (o0 + 2 * LAT_STRIDE)));
+        vo.v[m % NVB] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
     // Q K^T of tile kvt: S^T[key, row] for key score_key(0, half, i) of the tile, row l32, with
-    // the next tile's loads (8 latent rows and 1 rope load per wave) among the MFMAs.
-    auto qk_tile = [&](const char* kvt, const LaneOffs& lo, const TileSrc& src, char* nxt) __attribute__((always_inline)) {
+    // the next tile's loads (8 latent rows and 1 rope load per wave) among the MFMAs and, when
+    // a P V follows (PRE), its first V^T reads among the last MFMAs, which have no Q K^T reads
+    // left to overlap.
+    auto qk_tile = [&](const char* kvt, const LaneOffs& lo, const TileSrc& src, char* nxt, const char* kvp, VOps& vo,
+                       auto pre_tag) __attribute__((always_inline)) {
+        constexpr bool PRE = decltype(pre_tag)::value;
         bf16x8 qa[KB];
         auto rd = [&](int kb) __attribute__((always_inline)) {
             const char* ap = kb < KBL ? kvt + lo.lat + kb * 32 : kvt + lo.rope[kb - KBL];
@@ -377,13 +396,21 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
             if (kb + QK_AHEAD < KB) rd(kb + QK_AHEAD);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kb], qf[kb], s, 0, 0, 0);
         }
+        if constexpr (PRE) {
+#pragma unroll
+            for (int m = 0; m < PV_AHEAD_W; ++m) vread(vo, kvp, lo, m);
+        }
         // QK_AHEAD operand reads first, then per MFMA one read, and a load of the next tile
-        // after every fourth MFMA, so the vector memory pipe drains them under the matrix core.
+        // after every fourth MFMA, so the vector memory pipe drains them under the matrix core;
+        // the V^T reads (two per P V MFMA) go among the last MFMAs.
         __builtin_amdgcn_sched_group_barrier(0x100, QK_AHEAD, 0);
 #pragma unroll
         for (int k = 0; k < KB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (k + QK_AHEAD < KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (k + QK_AHEAD < KB)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            else if (PRE && k + QK_AHEAD - KB < PV_AHEAD_W)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             if (k % 4 == 0 && k / 4 < LAT_PER_WAVE + 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -393,31 +420,25 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
     // P V of the previous tile (kvp, probabilities pp) beside the softmax of this tile's scores
     // s: 32 MFMAs (16 column blocks x two 16-key halves), V^T reads PV_AHEAD_W MFMAs ahead, and
     // one piece of the softmax per MFMA, each chunk fenced so the interleave holds.
-    auto pv_softmax = [&](const char* kvp, const LaneOffs& lo, bf16x8 (&pp)[2], const f32x16& s, Softmax& sm,
-                          bf16x8 (&pn)[2], auto do_pv, auto do_soft) __attribute__((always_inline)) {
+    auto pv_softmax = [&](const char* kvp, const LaneOffs& lo, VOps& vo, bf16x8 (&pp)[2], const f32x16& s,
+                          Softmax& sm, bf16x8 (&pn)[2], auto do_pv, auto do_soft, auto pre_tag)
+        __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, SOFT = decltype(do_soft)::value;
+        constexpr bool PRE = decltype(pre_tag)::value;  // the first V^T reads were issued already
         constexpr int NM = 2 * NBO;
-        constexpr int NVB = PV_AHEAD_W + 1;
-        bf16x8 vv[NVB];
-        auto vread = [&](int m) __attribute__((always_inline)) {
-            const int h = m / NBO, d = m % NBO;
-            const char* vb = kvp + lo.v;
-            const int o0 = 16 * h * LAT_STRIDE + d * 64;
-            const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + o0));
-            const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + (o0 + 2 * LAT_STRIDE)));
-            vv[m % NVB] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (PV) {
             p_fence(pp);
+            if constexpr (!PRE) {
 #pragma unroll
-            for (int m = 0; m < PV_AHEAD_W; ++m) vread(m);
+                for (int m = 0; m < PV_AHEAD_W; ++m) vread(vo, kvp, lo, m);
+            }
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             if constexpr (PV) {
-                if (m + PV_AHEAD_W < NM) vread(m + PV_AHEAD_W);
-                pv_mfma(acc_o[m % NBO], vv[m % NVB], pp[m / NBO]);
+                if (m + PV_AHEAD_W < NM) vread(vo, kvp, lo, m + PV_AHEAD_W);
+                pv_mfma(acc_o[m % NBO], vo.v[m % NVB], pp[m / NBO]);
             }
             if constexpr (SOFT) sm.piece(m, s, m_ref, scale_log2, pn);
             __builtin_amdgcn_sched_barrier(0);
@@ -434,13 +455,14 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         __syncthreads();                     // ... and every wave's; buffer nxt is free
         const TileSrc src(lat, rope, tile_rows(kt + 1));  // clamped past the last tile
         const LaneOffs lo = lane_offs();
-        f32x16 s = qk_tile(cur, lo, src, nxt);
+        VOps vo;
+        f32x16 s = qk_tile(cur, lo, src, nxt, prv, vo, has_prev);
         // wave-uniform: a causal diagonal crosses this tile, or it is past the last one (the
         // branch touches only the scores, never O)
         if (kt * TK + TK - 1 > pmin || kt >= n_tiles) causal_mask(s, (kt < n_tiles ? pos - kt * TK : -1) - half);
         Softmax sm;
         bf16x8 pn[2];
-        pv_softmax(prv, lo, pprev, s, sm, pn, has_prev, std::true_type{});
+        pv_softmax(prv, lo, vo, pprev, s, sm, pn, has_prev, std::true_type{}, has_prev);
         m_ref = sm.mn;
         m_true = fmaxf(m_true, sm.mloc);
         over = over || sm.over;
@@ -454,7 +476,8 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         Softmax sm;
         bf16x8 pn[2];
         const f32x16 s{};
-        pv_softmax(kvp, lo, pprev, s, sm, pn, std::true_type{}, std::false_type{});
+        VOps vo;
+        pv_softmax(kvp, lo, vo, pprev, s, sm, pn, std::true_type{}, std::false_type{}, std::false_type{});
     };
 
     // Pass 0 against first-tile references; pass 1 only if some row of the workgroup passed

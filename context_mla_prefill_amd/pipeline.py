@@ -88,13 +88,28 @@ class RankInputs:
 
 
 def packed_rows(pl: DevicePlan, r: int) -> torch.Tensor:
-    """Row of each of rank r's local tokens in a packed per-request KV layout
-    (kv_start[request] + position): where its latent/rope source row sits in the inputs.
-    Equal to the plan's slots when the cache itself is packed."""
-    rows = pl.rank_rows(r)
-    gidx = pl.local_gidx[rows].long()
-    req = torch.searchsorted(pl.cu_glob.long(), gidx, right=True) - 1
-    return pl.kv_start.long()[req] + pl.positions[rows].long()
+    """Row of each of rank r's local tokens in the packed per-request KV layout of the inputs
+    (where its latent/rope source row sits): the slots pcp_partition writes for a packed
+    cache. A paged plan gets them from a packed twin plan of the same batch (same requests,
+    no block table), made once."""
+    if pl.block_table is None:
+        return pl.slot[pl.rank_rows(r)].long()
+    if getattr(pl, "_packed_twin", None) is None:
+        twin = alloc_plan(pl.q_lens.cpu().numpy(), pl.kv_lens.cpu().numpy(), pl.kv_start.cpu().numpy(), pl.P,
+                          device=pl.slot.device)
+        run_partition(twin)
+        pl._packed_twin = twin
+    return pl._packed_twin.slot[pl.rank_rows(r)].long()
+
+
+def cache_rows(q_lens, kv_lens, kv_start, block_table=None, device="cuda") -> torch.Tensor:
+    """Cache row of every key of every request (request-major, positions 0..kv_len-1): the
+    slots pcp_partition writes when every key is new and P = 1 (packed rows kv_start + j, or
+    rows through the block table). Set-up of a cache whose earlier keys are already in place."""
+    kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    pl = alloc_plan(kv, kv, kv_start, 1, device=device, block_table=block_table)
+    run_partition(pl)
+    return pl.slot.long()
 
 
 def rank_inputs(pl: DevicePlan, r: int, q_glob, latent_full, rope_full, topk_glob=None) -> RankInputs:

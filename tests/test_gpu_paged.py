@@ -403,3 +403,25 @@ def test_paged_block_ids_outside_the_cache(gpu_lib):
         bad = PagedSparseRun(ws, 504, workspace=workspace, table=(corrupt_table(bt, nb, 1), nb))
         assert torch.equal(good.bufs.o_cat[rows].view(torch.int16), bad.bufs.o_cat[rows].view(torch.int16))
         assert torch.equal(good.bufs.lse_cat[rows].view(torch.int32), bad.bufs.lse_cat[rows].view(torch.int32))
+
+
+def test_cache_rows_from_the_slot_map(gpu_lib):
+    """The set-up helper that places every key of a batch in a cache (the benchmark's paged
+    pre-fill, and the source rows of a paged plan's new tokens) takes its rows from the library's
+    slot map: bit-exact against the oracle's paged addressing and the packed rows."""
+    w = synth.custom(405, [300, 1, 70], [300, 900, 200], P=2, H=16, Dl=512, Dr=64)
+    bt, nb = make_block_table(w, 405)
+    reqs = np.concatenate([np.full(int(k), b, np.int64) for b, k in enumerate(w.kv_lens)])
+    poss = np.concatenate([np.arange(int(k), dtype=np.int64) for k in w.kv_lens])
+    got = pp.cache_rows(w.kv_lens, w.kv_lens, w.kv_start, block_table=bt).cpu().numpy()
+    assert np.array_equal(got, ok.paged_rows(bt, reqs, poss))
+    got = pp.cache_rows(w.kv_lens, w.kv_lens, w.kv_start).cpu().numpy()
+    assert np.array_equal(got, w.kv_start[reqs] + poss)
+    # a paged plan's new-token source rows come from its packed twin
+    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P, block_table=bt)
+    pp.run_partition(pl)
+    plan = hp.oracle_plan(w)
+    pos, req = hp.token_maps(plan)
+    for r, rp in enumerate(plan.ranks):
+        g = rp.local_gidx.astype(np.int64)
+        assert np.array_equal(pp.packed_rows(pl, r).cpu().numpy(), w.kv_start[req[g]] + pos[g])

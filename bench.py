@@ -66,7 +66,7 @@ def merge_bytes(merge_src: np.ndarray, H: int, Dv: int, kv_splits: int = 1) -> f
 
 
 # sources the dense attention kernel is compiled from (its traffic record names their hash)
-ATTN_SOURCES = ("attn_dense.hip", "attn_core.h")
+ATTN_SOURCES = ("attn_dense.hip", "attn_dense_wide.hip", "attn_core.h")
 
 
 def measured_traffic(workload: int):
@@ -179,6 +179,7 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--heads", type=int, default=0, help="query heads per GPU (default: the workload's)")
     ap.add_argument("--kv-splits", type=int, default=1,
                     help="cut every row's keys into this many ranges (split-KV partials, merged with the ranks)")
     ap.add_argument("--paged", action="store_true",
@@ -207,6 +208,8 @@ def main():
 
     _lib.load()
     w = synth.workload(args.workload)
+    if args.heads:  # a per-GPU share of the heads (e.g. 16 of 64 under TP4)
+        w = dataclasses.replace(w, H=args.heads)
     dev = "cuda"
     sparse = w.topk > 0
 

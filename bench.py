@@ -408,12 +408,12 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if sparse:
-        # algorithmic gather: every key of a query's set once per 64-head workgroup, as the
+        # algorithmic gather: every key of a query's set once per workgroup of up to 64 heads, as the
         # method stores it: the fp8 latent row, the bf16 rope row and the row's fp32 scale. The
         # workspace path reads a bf16 latent row instead (its own bytes, reported beside).
         alg_key = w.Dl + 2 * w.Dr + 4
         path_key = 2 * w.Dl + 2 * w.Dr if use_ws else alg_key
-        keys_r = [float(n_keys[g].sum()) * (w.H // 64) for g in gidx_r]
+        keys_r = [float(n_keys[g].sum()) * -(-w.H // 64) for g in gidx_r]
         gbs = float(np.mean([k * alg_key / (t * 1e-3) / 1e9 for k, t in zip(keys_r, t_rank)]))
         pbs = float(np.mean([k * path_key / (t * 1e-3) / 1e9 for k, t in zip(keys_r, t_rank)]))
         out["gather"] = {"bytes_per_key": alg_key, "bytes_per_rank": [round(k * alg_key) for k in keys_r],

@@ -197,8 +197,7 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: topk=%d outside 0..2048", a->topk);
         if (a->window < 0 || a->window > 4096)
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: window=%d outside 0..4096", a->window);
-        if (!big || a->H % 64 != 0)
-            return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path needs 512+64 dims and H %% 64 == 0");
+        if (!big) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path needs 512+64 dims");
         const int64_t max_kv = a->kv_dtype == MLA_KV_FP8_E4M3 ? kSparseMaxKv : kSparseMaxKvBf16;
         if (a->N_kv > max_kv)
             return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_partial: sparse path takes at most %d KV rows of this dtype",

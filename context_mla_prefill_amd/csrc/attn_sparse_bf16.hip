@@ -50,6 +50,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
         lse_out += wk.split * split_stride * H;
     }
     const int head = wk.hg * BM + pair * 32 + l32;
+    const bool valid = head < H;  // rows past H (a last head group under 64) stay idle
     const int64_t grow = (int64_t)wk.tok * H + head;
     // Buffer views of the latent and rope rows from row_base (the request's first row when
     // packed, the cache's first row when paged); the caller keeps N_kv * DL * 2 below 2^32.
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     {
         const __bf16* qrow = q + grow * S::DQK + 8 * half;
 #pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qrow + kb * 16);
+        for (int kb = 0; kb < S::KB; ++kb) qf[kb] = valid ? *reinterpret_cast<const bf16x8*>(qrow + kb * 16) : bf16x8{};
     }
     __syncthreads();
 
@@ -149,12 +150,12 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
         step(kv_lat1, kv_lat0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    write_rows<S, DL>(acc_o, m_ref, l_run, true, grow, wave, side, lane, ex, o_out, lse_out);
+    write_rows<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, o_out, lse_out);
 }
 
 template <bool PAGED>
 hipError_t launch_sparse_bf16(const mla_partial_args& a, hipStream_t stream) {
-    const int64_t grid = (int64_t)a.T_loc * (a.H / BM) * a.kv_splits;
+    const int64_t grid = (int64_t)a.T_loc * ((a.H + BM - 1) / BM) * a.kv_splits;
     hipLaunchKernelGGL((sparse_bf16_partial_kernel<512, 64, PAGED>), dim3((unsigned)grid), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H, a.N_kv,

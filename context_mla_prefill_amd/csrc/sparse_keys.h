@@ -7,8 +7,10 @@
 // range [key_lo, key_hi) count. ("[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid
 // KV and MegaMoE", "Purpose": sparse prefill attention under PCP.)
 //
-// A workgroup owns one token and 64 heads; its keys are visited in tiles of 64 slots: first the
-// selected indices in groups of 64, then the window.
+// A workgroup owns one token and a group of up to 64 heads (a head count that is not a multiple
+// of 64 leaves the last group's rows past H idle: their Q is zero and nothing is stored); its
+// keys are visited in tiles of 64 slots: first the selected indices in groups of 64, then the
+// window.
 #pragma once
 
 #include "attn_core.h"
@@ -30,8 +32,8 @@ __device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const in
                                                  const int32_t* __restrict__ positions,
                                                  const int32_t* __restrict__ vrow_kv_len) {
     SparseWork w;
-    // workgroup = (token, 64-head group, key split); splits of one row are adjacent
-    const int hg_count = H / BM;
+    // workgroup = (token, group of up to 64 heads, key split); splits of one row are adjacent
+    const int hg_count = (H + BM - 1) / BM;
     const int ridx = (int)blockIdx.x / kv_splits;
     w.split = (int)blockIdx.x - ridx * kv_splits;
     w.tok = ridx / hg_count;

@@ -269,9 +269,12 @@ typedef struct mla_partial_args {
  * kv_splits outside 1..64, split_stride < T_loc or no vrow_kv_len with kv_splits > 1,
  * block_table without vrow_req or with bt_stride < 1, paged N_kv not a multiple of 64,
  * T_loc > 0 with N_kv == 0);
- * UNSUPPORTED (dims other than 512+64 / 64+16, H, topk > 2048, window > 4096, sparse with
- * dims other than 512+64, with H not a multiple of 64, with fp8 KV of N_kv >= 2^23 rows or
- * bf16 KV of N_kv >= 2^22 rows (32-bit byte offsets), dense with fp8 KV, dtype); HIP.
+ * UNSUPPORTED (dims other than 512+64 / 64+16, H outside 1..128, topk > 2048, window > 4096,
+ * sparse with dims other than 512+64, with fp8 KV of N_kv >= 2^23 rows or bf16 KV of
+ * N_kv >= 2^22 rows (32-bit byte offsets), dense with fp8 KV, dtype); HIP.
+ * The sparse kernels run one token and a group of up to 64 heads per workgroup, so a head
+ * count under 64 (a per-GPU share of the heads under tensor parallelism) leaves the rest of
+ * the group's MFMA rows idle: H = 16 or 32 takes the time of H = 64.
  * Sparse preconditions: selected indices of a row are distinct; entries outside [0, p]
  * (including -1) are pads. */
 mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);

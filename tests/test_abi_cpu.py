@@ -101,8 +101,9 @@ def test_partial_validation_errors():
     assert call(_args(**ok, kv_dtype=_lib.MLA_KV_FP8_E4M3))[0] == _lib.MLA_ERR_UNSUPPORTED  # dense fp8
     assert call(_args(**ok, topk_idx=f, topk=4096, kv_dtype=1, kv_scale=f, H=64))[0] == _lib.MLA_ERR_UNSUPPORTED
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, H=64))[0] == _lib.MLA_ERR_INVALID_ARG  # no scale
-    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=16))[0] == _lib.MLA_ERR_UNSUPPORTED
-    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=96))[0] == _lib.MLA_ERR_UNSUPPORTED
+    # the sparse path takes any head count up to 128 (head groups of up to 64 rows); H above
+    # 128 is refused for both paths
+    assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=1, kv_scale=f, H=129))[0] == _lib.MLA_ERR_UNSUPPORTED
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64, N_kv=1 << 22))[0] == \
         _lib.MLA_ERR_UNSUPPORTED  # bf16 sparse rows addressed by 32-bit byte offsets
     assert call(_args(**ok, topk_idx=f, topk=2048, kv_dtype=0, H=64, D_latent=64, D_rope=16))[0] == \

@@ -4,6 +4,8 @@ Integer maps (partition, positions, slots, merge map) and the KV insert are bit-
 partial and merged O / LSE meet max|O-O_ref| <= 1e-2 and max|LSE-LSE_ref| <= 1e-3
 (3e-2 on O for the fp8 sparse workload), plus a relative-error sanity bound.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -701,5 +703,40 @@ def test_sparse128k_p2_workspace_sampled(gpu_lib):
     run = SparseRun(w, workspace=True)
     toks = hp.sample_tokens(w, run.plan)
     print(f"[check] sparse workload 4 on the workspace: {len(toks)} sampled tokens", flush=True)
+    run.check_values(toks)
+    assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())
+
+
+SPARSE_HEADS = {
+    # seed: (q_lens, kv_lens, P, H, topk, window)
+    231: ([1200, 1, 400], [1200, 900, 700], 2, 16, 256, 64),  # a per-GPU share under TP4 of 64 heads
+    232: ([900, 300], [900, 500], 2, 32, 192, 128),           # TP2
+    233: ([700], [700], 2, 80, 128, 64),                      # one full group and a partial one
+}
+
+
+@pytest.mark.parametrize("seed", sorted(SPARSE_HEADS))
+def test_sparse_head_counts_under_64(gpu_lib, seed):
+    """The sparse path at head counts that are not a multiple of 64 (per-GPU shares under
+    tensor parallelism): the last head group's rows past H stay idle. Every row of every rank
+    and the merge against the oracle, on both the in-kernel fp8 path and the bf16 workspace,
+    which agree bit for bit."""
+    q, kv, P, H, topk, window = SPARSE_HEADS[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64, topk=topk, window=window, kv_dtype="fp8",
+                     latent_std=1.0)
+    fp8 = SparseRun(w)
+    ws = SparseRun(w, workspace=True)
+    assert torch.equal(ws.bufs.o_cat.view(torch.int16), fp8.bufs.o_cat.view(torch.int16))
+    assert torch.equal(ws.bufs.lse_cat.view(torch.int32), fp8.bufs.lse_cat.view(torch.int32))
+    fp8.check_values(np.arange(w.T_glob))
+
+
+def test_sparse128k_p2_h16_workspace_sampled(gpu_lib):
+    """The 128K top-2048 workload at 16 heads (the per-GPU share of 64 heads under TP4) on the
+    workspace path: sampled tokens against the oracle, every row finite."""
+    w = dataclasses.replace(synth.workload(4), H=16)
+    run = SparseRun(w, workspace=True)
+    toks = hp.sample_tokens(w, run.plan)
+    print(f"[check] sparse workload 4 at 16 heads: {len(toks)} sampled tokens", flush=True)
     run.check_values(toks)
     assert bool(torch.isfinite(run.bufs.o_cat.float()).all()) and bool(torch.isfinite(run.bufs.lse_cat).all())

@@ -57,12 +57,23 @@ def sparse_set_sizes(topk_rows: np.ndarray, w) -> np.ndarray:
     return out
 
 
-def merge_bytes(merge_src: np.ndarray, H: int, Dv: int, kv_splits: int = 1) -> float:
-    """Bytes the merge must move: each contributor row (O bf16 + LSE fp32; one per rank row
-    and key split) read, each output row written, plus the map."""
-    n_contrib = int((merge_src >= 0).sum()) * kv_splits
+def merge_bytes(merge_src: np.ndarray, H: int, Dv: int, kv_splits: int = 1, ranges=None) -> float:
+    """Bytes the merge must move: each contributor row's LSE (fp32, every key split) and the O
+    (bf16) of each split that holds keys -- all kv_splits, or ranges[row] of them under a
+    per-row split plan -- read, each output row written, plus the map."""
+    src = merge_src[merge_src >= 0]
+    n_o = len(src) * kv_splits if ranges is None else int(ranges[src].sum())
     T, P = merge_src.shape
-    return float(n_contrib * H * (2 * Dv + 4) + T * H * (2 * Dv + 4) + T * P * 4)
+    return float(n_o * H * 2 * Dv + len(src) * kv_splits * H * 4 + T * H * (2 * Dv + 4) + T * P * 4)
+
+
+def row_ranges(pl, splits: np.ndarray) -> np.ndarray:
+    """Key ranges of every rank-concatenated partial row under a per-row split plan."""
+    out = np.empty(pl.T_total, np.int64)
+    for r in range(pl.P):
+        cu = pl.cu_q[r].cpu().numpy()
+        out[pl.rank_rows(r)] = np.repeat(splits[r], np.diff(cu))
+    return out
 
 
 # sources the dense attention kernel is compiled from (its traffic record names their hash)
@@ -182,6 +193,9 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="query heads per GPU (default: the workload's)")
     ap.add_argument("--kv-splits", type=int, default=1,
                     help="cut every row's keys into this many ranges (split-KV partials, merged with the ranks)")
+    ap.add_argument("--split-plan", action="store_true",
+                    help="with --kv-splits S: each virtual row gets its own range count (at most S) and the rows "
+                         "their launch order from the library's host planner (pcp_plan_splits)")
     ap.add_argument("--paged", action="store_true",
                     help="keep the KV in a paged cache of 64-row blocks (seeded random block table); the fp8 "
                          "workload then quantises its new bf16 rows on insert, in one call for all ranks")
@@ -283,16 +297,23 @@ def main():
             ri.latent = ri.rope = None
     S = args.kv_splits
     bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=S)
+    sp = pp.plan_splits(pl, w.H, w.Dl, S) if args.split_plan and S > 1 else None
+    plan_note = None
+    if sp is not None and sp.split_rows == 0:  # the planner splits nothing: launch unsplit
+        plan_note = f"per row (pcp_plan_splits, at most {S} ranges): no row split, launched unsplit"
+        sp, S = None, 1
+        bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=1)
     kv_dtype = _lib.MLA_KV_FP8_E4M3 if sparse else _lib.MLA_KV_BF16
     use_ws = sparse and not args.in_kernel_dequant
     if use_ws:  # the fp8 cache's blocks dequantised once per step into a bf16 workspace
         ws = torch.empty(n_cache, w.Dl, dtype=torch.bfloat16, device=dev)
         ws_blocks = torch.arange((n_cache + 63) // 64, dtype=torch.int32, device=dev)
         args_r = [pp.partial_args(pl, r, ranks[r], ws, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, topk=w.topk,
-                                  window=w.window, kv_splits=S) for r in range(w.P)]
+                                  window=w.window, kv_splits=S, split_plan=sp) for r in range(w.P)]
     else:
         args_r = [pp.partial_args(pl, r, ranks[r], kv_lat, kv_rope, bufs, w.H, w.Dl, w.Dr, w.scale, kv_dtype=kv_dtype,
-                                  kv_scale=kv_scale, topk=w.topk, window=w.window, kv_splits=S) for r in range(w.P)]
+                                  kv_scale=kv_scale, topk=w.topk, window=w.window, kv_splits=S, split_plan=sp)
+                  for r in range(w.P)]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -376,7 +397,8 @@ def main():
     t_insert = float(np.mean([events[k][w.P + 1][0].elapsed_time(events[k][w.P + 1][1]) for k in range(args.steps)]))
     avg_launch_ms = float(np.mean(t_rank))
     achieved = (flops_launch / w.P) / (avg_launch_ms * 1e-3) / 1e12
-    mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl, S)
+    mbytes = merge_bytes(pl.merge_src.cpu().numpy(), w.H, w.Dl, S,
+                         None if sp is None else row_ranges(pl, sp.splits.cpu().numpy()))
     att_traffic, merge_traffic = measured_traffic(args.workload) if not args.paged else (None, None)
 
     out = {
@@ -390,6 +412,9 @@ def main():
         "config": {"workload": w.name, "T": w.T_glob, "pcp": w.P, "heads": w.H, "d_latent": w.Dl,
                    "d_rope": w.Dr, "parallelism": f"{w.P} virtual PCP ranks, serial on 1 GPU",
                    **({"kv_splits": S} if S > 1 else {}),
+                   **({"split_plan": f"per row (pcp_plan_splits): {sp.split_rows} of {w.P * pl.n_vrows} "
+                                     "virtual rows split"} if sp is not None else {}),
+                   **({"split_plan": plan_note} if plan_note else {}),
                    **({"kv_cache": "paged, 64-row blocks" + (", fp8 quantise-on-insert" if quantise else "")}
                       if args.paged else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

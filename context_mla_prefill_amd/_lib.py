@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_PKG, "libmla_pcp.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, 1, 2, 3
 MLA_KV_BF16, MLA_KV_FP8_E4M3 = 0, 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ("mla_pcp_abi_version", "mla_pcp_last_error", "pcp_plan_sizes", "pcp_partition",
             "pcp_kv_insert", "pcp_kv_insert_fp8", "pcp_kv_dequant_fp8", "sparse_topk_select", "mla_prefill_partial",
-            "pcp_lse_merge")
+            "pcp_lse_merge", "pcp_plan_splits")
 
 _lib = None
 
@@ -48,6 +48,7 @@ class mla_partial_args(ctypes.Structure):
         ("scale", ctypes.c_float), ("o_partial", _p), ("lse", _p),
         ("kv_splits", _i32), ("split_stride", _i64), ("vrow_kv_len", _p),
         ("block_table", _p), ("bt_stride", _i32), ("vrow_req", _p),
+        ("vrow_splits", _p), ("vrow_order", _p),
     ]
 
 
@@ -80,6 +81,8 @@ def load():
     lib.mla_prefill_partial.restype = ctypes.c_int
     lib.mla_prefill_partial.argtypes = [ctypes.POINTER(mla_partial_args), _p]
     lib.pcp_lse_merge.restype = ctypes.c_int
+    lib.pcp_plan_splits.argtypes = [_pi32, _pi32, _i32, _i32, _i32, _i32, _i32, _i32, _pi32, _pi32]
+    lib.pcp_plan_splits.restype = ctypes.c_int
     lib.pcp_lse_merge.argtypes = [_p, _p, _p, _i32, _i64, _i32, _i32, _i64, _i32, _i64, _p, _p, _p, _p]
     if lib.mla_pcp_abi_version() != ABI_VERSION:
         raise RuntimeError(f"ABI mismatch: library {lib.mla_pcp_abi_version()} binding {ABI_VERSION}")
@@ -146,6 +149,20 @@ def pcp_plan_sizes(q_lens, kv_lens, P: int):
     return [int(x) for x in T_loc[:P]], int(nv.value), int(tg.value)
 
 
+def pcp_plan_splits(q_lens, kv_lens, P: int, H: int, D_latent: int, max_splits: int, n_workers: int):
+    """Host split-KV plan for the dense partials: (vrow_splits, vrow_order), int32 [P][n_vrows]."""
+    lib = load()
+    q = np.ascontiguousarray(q_lens, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_lens, dtype=np.int32)
+    _, n_vrows, _ = pcp_plan_sizes(q, kv, P)
+    splits = np.zeros((P, max(n_vrows, 1)), dtype=np.int32)
+    order = np.zeros((P, max(n_vrows, 1)), dtype=np.int32)
+    st = lib.pcp_plan_splits(q.ctypes.data_as(_pi32), kv.ctypes.data_as(_pi32), len(q), P, H, D_latent, max_splits,
+                             n_workers, splits.ctypes.data_as(_pi32), order.ctypes.data_as(_pi32))
+    _check(st, "pcp_plan_splits")
+    return splits[:, :n_vrows], order[:, :n_vrows]
+
+
 def pcp_partition(q_lens, kv_lens, kv_start, P, T_glob, n_vrows, T_loc_total, cu_seqlens_glob,
                   cu_seqlens_q, vrow_req, vrow_kv_start, vrow_kv_len, local_gidx, positions, slot,
                   merge_src, stream=None, block_table=None, bt_stride=0):
@@ -203,7 +220,8 @@ def sparse_topk_select(scores, ld, positions, T, k, topk_idx, stream=None):
 def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positions, n_vrows, T_loc, H,
                       D_latent, D_rope, scale, o_partial, lse, N_kv, kv_dtype=MLA_KV_BF16, kv_scale=None,
                       topk_idx=None, topk=0, window=0, kv_splits=1, split_stride=0,
-                      vrow_kv_len=None, block_table=None, bt_stride=0, vrow_req=None) -> mla_partial_args:
+                      vrow_kv_len=None, block_table=None, bt_stride=0, vrow_req=None, vrow_splits=None,
+                      vrow_order=None) -> mla_partial_args:
     rows = (split_stride * (kv_splits - 1) + T_loc) if kv_splits > 1 else T_loc
     eb = 2 if kv_dtype == MLA_KV_BF16 else 1
     _need(q, T_loc * H * (D_latent + D_rope) * 2, "mla_prefill_partial q")
@@ -215,6 +233,8 @@ def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positio
     _need(lse, rows * H * 4, "mla_prefill_partial lse")
     _need(cu_seqlens_q, (n_vrows + 1) * 4, "mla_prefill_partial cu_seqlens_q")
     _need(vrow_kv_start, n_vrows * 4, "mla_prefill_partial vrow_kv_start")
+    _need(vrow_splits, n_vrows * 4, "mla_prefill_partial vrow_splits")
+    _need(vrow_order, n_vrows * 4, "mla_prefill_partial vrow_order")
     if kv_dtype != MLA_KV_BF16:
         _need(kv_scale, (N_kv + 63) // 64 * 4, "mla_prefill_partial kv_scale")
     return mla_partial_args(
@@ -224,7 +244,7 @@ def make_partial_args(q, latent_kv, rope_k, cu_seqlens_q, vrow_kv_start, positio
         D_latent=D_latent, D_rope=D_rope, kv_dtype=kv_dtype, N_kv=N_kv, scale=float(scale),
         o_partial=_ptr(o_partial), lse=_ptr(lse), kv_splits=kv_splits, split_stride=split_stride,
         vrow_kv_len=_ptr(vrow_kv_len), block_table=_ptr(block_table), bt_stride=bt_stride,
-        vrow_req=_ptr(vrow_req))
+        vrow_req=_ptr(vrow_req), vrow_splits=_ptr(vrow_splits), vrow_order=_ptr(vrow_order))
 
 
 def mla_prefill_partial(args: mla_partial_args, stream=None):

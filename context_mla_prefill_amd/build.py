@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmla_pcp.so")
 
 SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense.hip", "attn_dense_wide.hip",
            "attn_sparse.hip",
-           "attn_sparse_bf16.hip", "topk_select.hip"]
+           "attn_sparse_bf16.hip", "topk_select.hip", "split_plan.hip"]
 
 # Per-file flags. The attention kernels keep O and the scores in VGPRs (MFMA VGPR form)
 # so its rare rescale is plain VALU work, leaving the AGPRs to Q.

@@ -31,9 +31,11 @@
 //    tile max exceeds it by more than kRescale (log2 units). Tiles that move no
 //    reference (nearly all of them) need no max exchange and no O rescale; a tile that
 //    does takes a workgroup-uniform slow path with one extra barrier.
-//  * Workgroups are launched longest-first (reverse of the flattened tile order), so
-//    the long late-chunk tiles start first and the short ones fill the tail.
+//  * Work order (work_order.h): virtual rows in the caller's order, else last row first;
+//    inside a row its tiles from the last to the first, so the long late-chunk tiles start
+//    first and the short ones fill the tail.
 #include "attn_core.h"
+#include "work_order.h"
 
 namespace mla {
 namespace {
@@ -74,55 +76,6 @@ struct DenseTile {
     static_assert(DQK % 16 == 0 && DL % 32 == 0 && DR % 8 == 0, "tile shape");
     static_assert(!WIDE || (LAT_LOADS % 4 == 0 && ROPE_LOADS % 4 == 0), "wide loads split evenly over 4 waves");
 };
-
-__device__ __forceinline__ int block_scan_incl(int v, int* sh) {
-    const int t = threadIdx.x;
-    sh[t] = v;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const int add = t >= off ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += add;
-        __syncthreads();
-    }
-    const int r = sh[t];
-    __syncthreads();
-    return r;
-}
-
-// Finds the (virtual row, tile) of this workgroup. Tiles are numbered longest-first:
-// virtual rows from last to first, and inside a row from its last tile to its first.
-__device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ cu, int n_vrows, int H,
-                                          int* sh, int& v_out, int& tile_out) {
-    __shared__ int s_v, s_tile, s_carry;
-    if (threadIdx.x == 0) {
-        s_v = -1;
-        s_tile = 0;
-        s_carry = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base < n_vrows; base += NT) {
-        const int k = base + threadIdx.x;
-        const int v = n_vrows - 1 - k;
-        int cnt = 0;
-        if (k < n_vrows) {
-            const int len = cu[v + 1] - cu[v];
-            cnt = len > 0 ? (int)(((int64_t)len * H + BM - 1) / BM) : 0;
-        }
-        const int incl = block_scan_incl(cnt, sh);
-        const int lo = s_carry + incl - cnt;
-        if (k < n_vrows && ridx >= lo && ridx < lo + cnt) {
-            s_v = v;
-            s_tile = cnt - 1 - (ridx - lo);
-        }
-        __syncthreads();
-        if (threadIdx.x == NT - 1) s_carry += incl;
-        __syncthreads();
-        if (s_v >= 0) break;
-    }
-    v_out = s_v;
-    tile_out = s_tile;
-}
 
 // Wide shape: buffer views of the rows of KV tile kt. The base is the tile's first row,
 // clamped to the last valid row (the loads issued after the final tile read that row into
@@ -203,7 +156,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const int32_t* __restrict__ positions, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out, int kv_splits, int64_t split_stride,
     const int32_t* __restrict__ vrow_kv_len, const int32_t* __restrict__ block_table, int bt_stride,
-    const int32_t* __restrict__ vrow_req) {
+    const int32_t* __restrict__ vrow_req, const int32_t* __restrict__ vrow_splits,
+    const int32_t* __restrict__ vrow_order) {
     using T = DenseTile<DL, DR>;
     __shared__ __attribute__((aligned(1024))) char kv_lds0[T::TILE_BYTES];  // KV tile double buffer:
     __shared__ __attribute__((aligned(1024))) char kv_lds1[T::TILE_BYTES];  // two separate objects
@@ -213,13 +167,10 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     __shared__ int s_maxpos[NT / 64];
     int* sh = reinterpret_cast<int*>(&Px[0][0][0]);  // scan scratch, used before the KV loop only
 
-    // workgroup = (row tile, key split); splits of one tile are adjacent in launch order
-    const int ridx = (int)blockIdx.x / kv_splits;
-    const int split = (int)blockIdx.x - ridx * kv_splits;
-    int v, tile;
-    find_tile(ridx, cu, n_vrows, H, sh, v, tile);
-    v = __builtin_amdgcn_readfirstlane(v);  // workgroup-uniform: keep it in SGPRs
-    tile = __builtin_amdgcn_readfirstlane(tile);
+    // workgroup = (virtual row, row tile, key range)
+    const sched::DenseWork wk =
+        sched::find_work<BM, NT>((int)blockIdx.x, cu, n_vrows, H, vrow_splits, vrow_order, kv_splits, sh);
+    const int v = wk.v, tile = wk.tile, split = wk.split;
     if (v < 0) return;
 
     const int tid = threadIdx.x;
@@ -259,10 +210,13 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     kv_hi = kv_hi + 1;
     // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
     int key_lo = 0;
+    if (wk.nsplit > 1) {
+        int key_hi;
+        sched::split_range(vrow_kv_len[v], split, wk.nsplit, key_lo, key_hi);
+        kv_hi = min(kv_hi, key_hi);
+    }
+    float* const lse0 = lse_out;
     if (kv_splits > 1) {
-        const int n = (vrow_kv_len[v] + BN - 1) / BN;
-        key_lo = BN * (int)((unsigned)split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
-        kv_hi = min(kv_hi, BN * (int)((unsigned)(split + 1) * n / kv_splits));
         o_out += split * split_stride * H * DL;
         lse_out += split * split_stride * H;
     }
@@ -518,6 +472,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
         }
         if (side == 0 && half == 0) lse_out[grow] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
+    sched::mark_empty_slices(lse0, grow, valid && side == 0 && half == 0, split, wk.nsplit, kv_splits,
+                             split_stride, H);
 }
 
 template <int DL, int DR, bool PAGED>
@@ -527,7 +483,7 @@ hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
                        (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.n_vrows, a.H, a.N_kv, a.scale * kLog2e,
                        (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len, a.block_table,
-                       a.bt_stride, a.vrow_req);
+                       a.bt_stride, a.vrow_req, a.kv_splits > 1 ? a.vrow_splits : nullptr, a.vrow_order);
     return hipGetLastError();
 }
 

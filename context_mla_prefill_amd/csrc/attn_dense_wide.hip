@@ -33,10 +33,13 @@
 //    copy of the step, chosen once per tile).
 //  * The P V MFMAs are issued as inline asm so that O can live in AGPRs while the scores use
 //    the MFMA's VGPR form (the compiler picks one accumulator form per function).
-//  * Workgroups are launched longest-first (reverse of the flattened tile order).
+//  * Work order (work_order.h): virtual rows in the caller's order, else last row first; inside
+//    a row its tiles from the last (longest key range) to the first, the key ranges of one
+//    tile adjacent when the row's keys are split.
 #include <type_traits>
 
 #include "attn_core.h"
+#include "work_order.h"
 
 namespace mla {
 namespace {
@@ -57,55 +60,6 @@ constexpr int LAT_PER_WAVE = TK / 4;  // 8 latent row loads per wave and tile
 constexpr int QK_AHEAD = 4;           // Q K^T operand reads in flight
 constexpr int PV_AHEAD_W = 2;         // P V MFMAs' worth of V^T reads in flight
 constexpr float kRefSlack = 32.0f;    // log2 headroom of the fixed reference
-
-__device__ __forceinline__ int block_scan_incl(int v, int* sh) {
-    const int t = threadIdx.x;
-    sh[t] = v;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const int add = t >= off ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += add;
-        __syncthreads();
-    }
-    const int r = sh[t];
-    __syncthreads();
-    return r;
-}
-
-// (virtual row, row tile) of workgroup ridx, tiles numbered longest-first: virtual rows from
-// last to first, inside a row from its last tile to its first.
-__device__ __forceinline__ void find_tile(int ridx, const int32_t* __restrict__ cu, int n_vrows, int H, int* sh,
-                                          int& v_out, int& tile_out) {
-    __shared__ int s_v, s_tile, s_carry;
-    if (threadIdx.x == 0) {
-        s_v = -1;
-        s_tile = 0;
-        s_carry = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base < n_vrows; base += NT) {
-        const int k = base + threadIdx.x;
-        const int v = n_vrows - 1 - k;
-        int cnt = 0;
-        if (k < n_vrows) {
-            const int len = cu[v + 1] - cu[v];
-            cnt = len > 0 ? (int)(((int64_t)len * H + WBM - 1) / WBM) : 0;
-        }
-        const int incl = block_scan_incl(cnt, sh);
-        const int lo = s_carry + incl - cnt;
-        if (k < n_vrows && ridx >= lo && ridx < lo + cnt) {
-            s_v = v;
-            s_tile = cnt - 1 - (ridx - lo);
-        }
-        __syncthreads();
-        if (threadIdx.x == NT - 1) s_carry += incl;
-        __syncthreads();
-        if (s_v >= 0) break;
-    }
-    v_out = s_v;
-    tile_out = s_tile;
-}
 
 // Where the keys of one tile live: KV row of its first key and how many keys it has.
 struct TileRows {
@@ -225,7 +179,8 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start, const int32_t* __restrict__ positions,
     int n_vrows, int H, int64_t N_kv, float scale_log2, __bf16* __restrict__ o_out, float* __restrict__ lse_out,
     int kv_splits, int64_t split_stride, const int32_t* __restrict__ vrow_kv_len,
-    const int32_t* __restrict__ block_table, int bt_stride, const int32_t* __restrict__ vrow_req) {
+    const int32_t* __restrict__ block_table, int bt_stride, const int32_t* __restrict__ vrow_req,
+    const int32_t* __restrict__ vrow_splits, const int32_t* __restrict__ vrow_order) {
     // KV tile buffers: three separate LDS objects, so the compiler can tell that loads streaming
     // into one never touch the others and does not wait for them before reading a tile.
     __shared__ __attribute__((aligned(1024))) char kv0[TILE_BYTES];
@@ -235,13 +190,10 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
     __shared__ int s_maxpos[NT / 64];
     __shared__ int s_redo[NT / 64];
 
-    // workgroup = (row tile, key split); splits of one tile are adjacent in launch order
-    const int ridx = (int)blockIdx.x / kv_splits;
-    const int split = (int)blockIdx.x - ridx * kv_splits;
-    int v, tile;
-    find_tile(ridx, cu, n_vrows, H, sh, v, tile);
-    v = __builtin_amdgcn_readfirstlane(v);
-    tile = __builtin_amdgcn_readfirstlane(tile);
+    // workgroup = (virtual row, row tile, key range)
+    const sched::DenseWork wk =
+        sched::find_work<WBM, NT>((int)blockIdx.x, cu, n_vrows, H, vrow_splits, vrow_order, kv_splits, sh);
+    const int v = wk.v, tile = wk.tile, split = wk.split;
     if (v < 0) return;
 
     const int tid = threadIdx.x;
@@ -278,10 +230,13 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
     // Key range of this split: whole 64-key blocks of the request's KV (the split rule does not
     // depend on the kernel's tile size).
     int key_lo = 0;
+    if (wk.nsplit > 1) {
+        int key_hi;
+        sched::split_range(vrow_kv_len[v], split, wk.nsplit, key_lo, key_hi);
+        kv_hi = min(kv_hi, key_hi);
+    }
+    float* const lse0 = lse_out;
     if (kv_splits > 1) {
-        const int n = (vrow_kv_len[v] + 63) / 64;
-        key_lo = 64 * (int)((unsigned)split * n / kv_splits);  // n <= 2^25 blocks, kv_splits <= 64
-        kv_hi = min(kv_hi, 64 * (int)((unsigned)(split + 1) * n / kv_splits));
         o_out += split * split_stride * H * DL;
         lse_out += split * split_stride * H;
     }
@@ -538,6 +493,7 @@ __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(
         }
         if (half == 0) lse_out[grow] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
+    sched::mark_empty_slices(lse0, grow, valid && half == 0, split, wk.nsplit, kv_splits, split_stride, H);
 }
 
 template <bool PAGED>
@@ -546,7 +502,8 @@ hipError_t launch_wide(const mla_partial_args& a, hipStream_t stream) {
     hipLaunchKernelGGL((dense_wide_kernel<PAGED>), dim3((unsigned)grid), dim3(NT), 0, stream, (const __bf16*)a.q,
                        (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q, a.vrow_kv_start, a.positions,
                        a.n_vrows, a.H, a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse, a.kv_splits,
-                       a.split_stride, a.vrow_kv_len, a.block_table, a.bt_stride, a.vrow_req);
+                       a.split_stride, a.vrow_kv_len, a.block_table, a.bt_stride, a.vrow_req,
+                       a.kv_splits > 1 ? a.vrow_splits : nullptr, a.vrow_order);
     return hipGetLastError();
 }
 

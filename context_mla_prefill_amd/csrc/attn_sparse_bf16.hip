@@ -26,7 +26,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     const int32_t* __restrict__ topk_idx, int topk, int window, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out, int kv_splits, int64_t split_stride,
     const int32_t* __restrict__ vrow_kv_len, const int32_t* __restrict__ block_table, int bt_stride,
-    const int32_t* __restrict__ vrow_req) {
+    const int32_t* __restrict__ vrow_req,
+    const int32_t* __restrict__ vrow_splits) {
     using S = Shape<DL, DR>;
     static_assert(DL * 2 == 1024, "one direct-to-LDS load per 1024-byte latent row");
     constexpr int LAT_PER_WAVE = BN / 4;  // latent row loads per wave and tile
@@ -37,7 +38,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     __shared__ int win_blk[MAX_WINDOW / BN + 1];
     __shared__ Exchange ex;
 
-    const SparseWork wk = sparse_work(H, kv_splits, cu, n_vrows, vrow_kv_start, positions, vrow_kv_len);
+    const SparseWork wk =
+        sparse_work(H, kv_splits, cu, n_vrows, vrow_kv_start, positions, vrow_kv_len, vrow_splits);
+    if (wk.split >= wk.nsplit) return;  // a range past the row's count: no keys, nothing to write
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int pair = wave >> 1;
@@ -45,6 +48,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     const int lane = tid & 63;
     const int half = lane >> 5;
     const int l32 = lane & 31;
+    float* const lse0 = lse_out;
     if (kv_splits > 1) {
         o_out += wk.split * split_stride * H * DL;
         lse_out += wk.split * split_stride * H;
@@ -151,6 +155,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     write_rows<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, o_out, lse_out);
+    sched::mark_empty_slices(lse0, grow, valid && side == 0 && half == 0, wk.split, wk.nsplit, kv_splits,
+                             split_stride, H);
 }
 
 template <bool PAGED>
@@ -160,7 +166,8 @@ hipError_t launch_sparse_bf16(const mla_partial_args& a, hipStream_t stream) {
                        (const __bf16*)a.q, (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q,
                        a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H, a.N_kv,
                        a.scale * kLog2e, (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len,
-                       a.block_table, a.bt_stride, a.vrow_req);
+                       a.block_table, a.bt_stride, a.vrow_req,
+                       a.kv_splits > 1 ? a.vrow_splits : nullptr);
     return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@
 // Its first threads turn the token's contributor LSEs and the sinks into per-(contributor,
 // head) weights in LDS; then the workgroup streams the group's output elements, 16 bytes per
 // thread and UNROLL vectors in flight, reading each contributor's rows (contiguous bf16) with
-// full-width coalesced non-temporal loads (every byte is read exactly once).
+// full-width coalesced non-temporal loads (every byte is read at most once; a contributor
+// whose weight is zero is not read).
 #include <math.h>
 
 #include "internal.h"
@@ -91,18 +92,20 @@ __global__ __launch_bounds__(NT) void merge_kernel(
         for (int k = 0; k < n; ++k) {
             const u32x4* src = src_base + (int64_t)rows[k] * V;
             u32x4 raw[UNROLL];
+            float w[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
                 const int v = v0 + u * NT;
-                raw[u] = v < V_hi ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
+                w[u] = v < V_hi ? wts(k, v / G) : 0.0f;
+                // a zero weight (LSE -inf: an empty key range, or a slice the row does not use)
+                // reads nothing: such a slice's output may never have been written
+                raw[u] = w[u] != 0.0f ? __builtin_nontemporal_load(src + v) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) {
-                const int v = v0 + u * NT;
-                const float w = v < V_hi ? wts(k, v / G) : 0.0f;
                 const bf16x8 x = __builtin_bit_cast(bf16x8, raw[u]);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[u][j] += w * (float)x[j];
+                for (int j = 0; j < 8; ++j) acc[u][j] += w[u] * (float)x[j];
             }
         }
 #pragma unroll

@@ -14,6 +14,7 @@
 #pragma once
 
 #include "attn_core.h"
+#include "work_order.h"
 
 namespace mla {
 namespace attn {
@@ -21,16 +22,20 @@ namespace attn {
 constexpr int MAX_TOPK = 2048;
 constexpr int MAX_WINDOW = 4096;
 
-// The workgroup's token, head group and key split, its virtual row and the split's key range.
+// The workgroup's token, head group and key split, its virtual row, the row's number of key
+// ranges and the split's key range.
 struct SparseWork {
-    int tok, hg, split, lo_v, p, key_lo, key_hi;
+    int tok, hg, split, nsplit, lo_v, p, key_lo, key_hi;
     int64_t kv0;
 };
 
+// Grid: (token, head group, split < kv_splits); a workgroup whose split is not below its row's
+// range count (nsplit) has no work.
 __device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const int32_t* __restrict__ cu, int n_vrows,
                                                  const int32_t* __restrict__ vrow_kv_start,
                                                  const int32_t* __restrict__ positions,
-                                                 const int32_t* __restrict__ vrow_kv_len) {
+                                                 const int32_t* __restrict__ vrow_kv_len,
+                                                 const int32_t* __restrict__ vrow_splits) {
     SparseWork w;
     // workgroup = (token, group of up to 64 heads, key split); splits of one row are adjacent
     const int hg_count = (H + BM - 1) / BM;
@@ -48,13 +53,10 @@ __device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const in
     w.kv0 = vrow_kv_start[lo_v];
     w.p = positions[w.tok];
     // Key range of this split: whole 64-key tiles [key_lo, key_hi) of the request's KV.
+    w.nsplit = sched::row_splits(vrow_splits, lo_v, kv_splits);
     w.key_lo = 0;
     w.key_hi = INT32_MAX;
-    if (kv_splits > 1) {
-        const int n = (vrow_kv_len[lo_v] + BN - 1) / BN;
-        w.key_lo = BN * (int)((unsigned)w.split * n / kv_splits);  // n <= 2^25 tiles, kv_splits <= 64
-        w.key_hi = BN * (int)((unsigned)(w.split + 1) * n / kv_splits);
-    }
+    if (w.nsplit > 1) sched::split_range(vrow_kv_len[lo_v], w.split, w.nsplit, w.key_lo, w.key_hi);
     return w;
 }
 

@@ -140,9 +140,36 @@ def alloc_step(pl: DevicePlan, H: int, Dl: int, device="cuda", kv_splits: int = 
                        lse=torch.empty(pl.T_glob, H, dtype=torch.float32, device=device))
 
 
+@dataclass
+class SplitPlan:
+    """Per-row split KV for the dense partials (pcp_plan_splits), on the device."""
+    max_splits: int
+    splits: torch.Tensor  # [P, n_vrows] key ranges of each virtual row
+    order: torch.Tensor  # [P, n_vrows] order in which the workgroups take the rows
+
+    @property
+    def split_rows(self) -> int:
+        return int((self.splits > 1).sum())
+
+
+def plan_splits(pl: DevicePlan, H: int, Dl: int, max_splits: int, n_workers: int | None = None,
+                device="cuda") -> SplitPlan:
+    """Host planning of the per-row key-range counts (set-up; the host knows the lengths)."""
+    if n_workers is None:
+        n_workers = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+    splits, order = _lib.pcp_plan_splits(pl.q_lens.cpu().numpy(), pl.kv_lens.cpu().numpy(), pl.P, H, Dl,
+                                         max_splits, n_workers)
+    return SplitPlan(max_splits=max_splits, splits=torch.from_numpy(splits).to(device),
+                     order=torch.from_numpy(order).to(device))
+
+
 def partial_args(pl: DevicePlan, r: int, ri: RankInputs, kv_latent, kv_rope, bufs: StepBuffers, H, Dl, Dr,
-                 scale, kv_dtype=_lib.MLA_KV_BF16, kv_scale=None, topk=0, window=0, kv_splits=1):
+                 scale, kv_dtype=_lib.MLA_KV_BF16, kv_scale=None, topk=0, window=0, kv_splits=1,
+                 split_plan: SplitPlan | None = None):
+    """Arguments of rank r's mla_prefill_partial; with split_plan, kv_splits must be its max_splits."""
     rows = pl.rank_rows(r)
+    if split_plan is not None:
+        assert kv_splits == split_plan.max_splits, "kv_splits must match the split plan"
     return _lib.make_partial_args(
         q=ri.q, latent_kv=kv_latent, rope_k=kv_rope, cu_seqlens_q=pl.cu_q[r], vrow_kv_start=pl.vrow_kv_start[r],
         positions=pl.positions[rows], n_vrows=pl.n_vrows, T_loc=pl.T_loc[r], H=H, D_latent=Dl, D_rope=Dr,
@@ -151,7 +178,9 @@ def partial_args(pl: DevicePlan, r: int, ri: RankInputs, kv_latent, kv_rope, buf
         kv_splits=kv_splits, split_stride=pl.T_total if kv_splits > 1 else 0,
         vrow_kv_len=pl.vrow_kv_len[r] if kv_splits > 1 else None, block_table=pl.block_table,
         bt_stride=0 if pl.block_table is None else int(pl.block_table.shape[1]),
-        vrow_req=None if pl.block_table is None else pl.vrow_req[r])
+        vrow_req=None if pl.block_table is None else pl.vrow_req[r],
+        vrow_splits=None if split_plan is None else split_plan.splits[r],
+        vrow_order=None if split_plan is None else split_plan.order[r])
 
 
 def run_merge(pl: DevicePlan, bufs: StepBuffers, sink, H: int, Dl: int, stream=None, kv_splits: int = 1):

@@ -130,6 +130,14 @@ def _config6_lengths() -> tuple[np.ndarray, np.ndarray]:
     return q.astype(np.int32), kv.astype(np.int32)
 
 
+def _config7_lengths() -> tuple[np.ndarray, np.ndarray]:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([7, T_LENGTHS, 0])))
+    ctx = np.floor(np.exp(rng.uniform(math.log(32768), math.log(131072), 64))).astype(np.int64)
+    q = np.array([4096] + [1] * 64, dtype=np.int64)
+    kv = np.concatenate([[4096], ctx])
+    return q.astype(np.int32), kv.astype(np.int32)
+
+
 def workload(cfg: int) -> Workload:
     if cfg == 1:
         return Workload(1, "tiny dense T=256 P=2 H=4 64+16", [256], [256], P=2, H=4, Dl=64, Dr=16)
@@ -147,6 +155,10 @@ def workload(cfg: int) -> Workload:
         q, kv = _config6_lengths()
         return Workload(6, "chunked prefill step 32768 tokens (continuations + decode) P=4 H=16 512+64", q, kv,
                         P=4, H=16, Dl=512, Dr=64)
+    if cfg == 7:
+        q, kv = _config7_lengths()
+        return Workload(7, "decode-heavy: 64 decode rows over 32K-128K contexts + 4096-token prefill P=4 H=16 512+64",
+                        q, kv, P=4, H=16, Dl=512, Dr=64)
     raise ValueError(f"unknown workload {cfg}")
 
 

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define MLA_PCP_ABI_VERSION 5
+#define MLA_PCP_ABI_VERSION 6
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -222,15 +222,19 @@ mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* po
  * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]) (row = KV row, so
  *   with paging one scale per block), dequantised inside the sparse kernel. A sparse call with
  *   bf16 latent (for instance the workspace of pcp_kv_dequant_fp8) gathers bf16 rows instead.
- * Split KV (kv_splits = S > 1): the key set of a row is cut by key position into S
- *   ranges and each range gives its own partial (O, LSE), written at split slice s of
- *   the outputs; merging the S partials (pcp_lse_merge with the same S) gives the
- *   unsplit result. With L = vrow_kv_len[v] and n = ceil(L / 64) tiles, range s holds
- *   request-relative keys [64 * floor(s * n / S), 64 * floor((s + 1) * n / S)), the
- *   last one ending at L. A range with no key of the row gives O = 0, LSE = -inf. The
- *   per-rank partial of the "local partial, global LSE merge" reading ("[DeepSeekV4][PCP]
- *   Enable context-parallel prefill for hybrid KV and MegaMoE", "Purpose") applied to
- *   key ranges instead of ranks: long rows are spread over more workgroups.
+ * Split KV (kv_splits = S > 1): the key set of virtual row v is cut by key position into
+ *   s_v ranges (s_v = vrow_splits[v], or S for every row when vrow_splits is NULL) and
+ *   each range gives its own partial (O, LSE), written at split slice s of the outputs;
+ *   merging the slices (pcp_lse_merge with the same S) gives the unsplit result. With
+ *   L = vrow_kv_len[v] and n = ceil(L / 64) tiles, range s holds request-relative keys
+ *   [64 * floor(s * n / s_v), 64 * floor((s + 1) * n / s_v)), the last one ending at L.
+ *   A range with no key of the row gives O = 0, LSE = -inf. Slices s_v .. S-1 of the
+ *   row's tokens get LSE = -inf and their O is left as it was (the merge does not read
+ *   an output whose weight is zero). The per-rank partial of the "local partial, global
+ *   LSE merge" reading ("[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid KV
+ *   and MegaMoE", "Purpose") applied to key ranges instead of ranks: long rows, such as
+ *   decode rows over a long context, are spread over more workgroups (pcp_plan_splits
+ *   picks the per-row counts).
  */
 typedef struct mla_partial_args {
     const void* q;               /* device bf16 [T_loc][H][D_latent + D_rope]            */
@@ -263,6 +267,12 @@ typedef struct mla_partial_args {
     const int32_t* block_table;  /* device [n_req][bt_stride] or NULL (packed KV)          */
     int32_t bt_stride;           /* entries per request row of block_table                 */
     const int32_t* vrow_req;     /* device [n_vrows] request of each virtual row (paged)   */
+    const int32_t* vrow_splits;  /* device [n_vrows] key ranges of each virtual row, clamped
+                                    into 1..kv_splits, or NULL (every row kv_splits);
+                                    ignored when kv_splits == 1                          */
+    const int32_t* vrow_order;   /* device [n_vrows] order in which workgroups take the
+                                    virtual rows (a permutation; entries are clamped into
+                                    [0, n_vrows)), or NULL (last row first). Dense only. */
 } mla_partial_args;
 
 /* Errors: INVALID_ARG (null pointers, sizes, 16-byte misalignment, fp8 without scales,
@@ -278,6 +288,34 @@ typedef struct mla_partial_args {
  * Sparse preconditions: selected indices of a row are distinct; entries outside [0, p]
  * (including -1) are pads. */
 mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
+
+/*
+ * pcp_plan_splits — host-only choice of split KV for the dense partials: the number of key
+ * ranges of every virtual row and the order in which the workgroups take the rows, for
+ * mla_partial_args.vrow_splits / vrow_order (copied to the device by the caller).
+ * Source: the per-rank partials and global LSE merge of "[DeepSeekV4][PCP] Enable
+ * context-parallel prefill for hybrid KV and MegaMoE", "Purpose", applied to key ranges, so
+ * long rows (decode rows over a long context are replicated on every rank: "[Core] Add MRV2
+ * virtual-batch PCP for MLA", "PCP algorithm") are spread over several workgroups.
+ * A scheduling heuristic, not part of the method: every (row tile, key range) work item is
+ * costed as its key count plus a fixed per-workgroup cost, items are dealt in launch order
+ * to n_workers units (each to the first that falls idle), and the plan with the shortest
+ * modelled finish time is returned; a plan that splits must beat the unsplit one by 2 %,
+ * else every row gets 1 and the default order. Rows never get more than max_splits ranges.
+ *
+ *  q_lens, kv_lens  host int32 [n_req] as for pcp_plan_sizes; P as there.
+ *  H, D_latent      query heads (1..128) and latent width (512 or 64) of the launch.
+ *  max_splits       the kv_splits the launch will use (1..64).
+ *  n_workers        workgroups resident at once: the GPU's compute units (one dense
+ *                   workgroup per unit; 256 on MI355X).
+ *  vrow_splits      host out int32 [P][n_vrows]: ranges of each virtual row (1..max_splits).
+ *  vrow_order       host out int32 [P][n_vrows]: per rank, a permutation of its rows.
+ * Errors: as pcp_plan_sizes; INVALID_ARG (H, max_splits, n_workers, null outputs);
+ * UNSUPPORTED (D_latent).
+ */
+mla_status pcp_plan_splits(const int32_t* q_lens, const int32_t* kv_lens, int32_t n_req, int32_t P,
+                           int32_t H, int32_t D_latent, int32_t max_splits, int32_t n_workers,
+                           int32_t* vrow_splits, int32_t* vrow_order);
 
 /*
  * pcp_lse_merge — merge per-rank partials into global token order with the sink once.
@@ -296,7 +334,9 @@ mla_status mla_prefill_partial(const mla_partial_args* args, void* stream);
  *                                           [0, R_total) are ignored.
  *  sink      device fp32 [H] or NULL (no sink).
  *  o_out     device bf16 out [T_glob][H][D_v]; lse_out device fp32 [T_glob][H] or NULL.
- * A row with no contributor gets O = 0 and LSE = s_h (-inf without a sink).
+ * A row with no contributor gets O = 0 and LSE = s_h (-inf without a sink). A contributor
+ * slice whose weight exp(L_k - M) / D is zero (L_k = -inf: an empty key range, or a slice
+ * its row does not use under per-row split KV) is not read, so its O may hold anything.
  * Errors: INVALID_ARG (null, sizes, P out of 1..64, kv_splits < 1, P * kv_splits above
  * 64, split_stride < 0, misalignment); UNSUPPORTED (D_v not a multiple of 8 in 8..1024,
  * H above 128); HIP.

@@ -31,6 +31,12 @@ def host_bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def poison_partials(bufs):
+    """NaN in every partial output and LSE before the kernels run."""
+    bufs.o_cat.view(torch.int16).fill_(0x7FC0)
+    bufs.lse_cat.fill_(float("nan"))
+
+
 def check_plan(pl, plan):
     """Bit-exact comparison of the device plan with the oracle's partition."""
     torch.cuda.synchronize()
@@ -52,9 +58,13 @@ def check_plan(pl, plan):
 class DenseRun:
     """Runs partition -> insert -> P partials -> merge for a bf16 dense workload."""
 
-    def __init__(self, w, kv_splits=1):
+    def __init__(self, w, kv_splits=1, split_plan=None):
+        """split_plan: per-row split KV (pipeline.SplitPlan, max_splits == kv_splits); the
+        partial buffers then start as NaN, so a slice the kernels leave unwritten and the merge
+        read would poison the result."""
         self.w = w
         self.kv_splits = kv_splits
+        self.split_plan = split_plan
         self.plan = hp.oracle_plan(w)
         print(f"[run] workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv} kv_splits={kv_splits}", flush=True)
         self.q_bits = synth.q_rows(w)
@@ -71,6 +81,8 @@ class DenseRun:
         self.kv_lat.view(torch.int16)[new_rows] = 0x7FC0
         self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
         self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
+        if split_plan is not None:
+            poison_partials(self.bufs)
         self.sink_d = torch.from_numpy(self.sink).cuda()
         ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full) for r in range(w.P)]
         # every rank's rows reach the full KV (the all-gather) before any rank attends
@@ -79,7 +91,7 @@ class DenseRun:
                                _lib.MLA_KV_BF16, w.N_kv, self.kv_lat, self.kv_rope)
         for r, ri in enumerate(ranks):
             args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                   kv_splits=kv_splits)
+                                   kv_splits=kv_splits, split_plan=split_plan)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
@@ -347,11 +359,14 @@ SPARSE_O_TOL = 3e-2
 class SparseRun:
     """partition -> fp8 insert -> P sparse partials -> merge for an fp8 top-k workload."""
 
-    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None, kv_splits=1, workspace=False):
+    def __init__(self, w, lat_codes=None, kv_scale=None, topk_rows=None, kv_splits=1, workspace=False,
+                 split_plan=None):
         """workspace: dequantise the cache once into a bf16 workspace (pcp_kv_dequant_fp8) and
-        run the sparse partials on bf16 rows instead of dequantising inside the kernel."""
+        run the sparse partials on bf16 rows instead of dequantising inside the kernel.
+        split_plan: per-row split KV, partial buffers poisoned first (as DenseRun)."""
         self.w = w
         self.kv_splits = kv_splits
+        self.split_plan = split_plan
         self.workspace = workspace
         self.plan = hp.oracle_plan(w)
         print(f"[run] sparse workload {w.cfg} {w.name} T={w.T_glob} N_kv={w.N_kv}", flush=True)
@@ -374,6 +389,8 @@ class SparseRun:
         self.kv_lat[new_rows] = 0x7F
         self.kv_rope.view(torch.int16)[new_rows] = 0x7FC0
         self.bufs = pp.alloc_step(pl, w.H, w.Dl, kv_splits=kv_splits)
+        if split_plan is not None:
+            poison_partials(self.bufs)
         self.sink_d = torch.from_numpy(self.sink).cuda()
         ranks = [pp.rank_inputs(pl, r, q, lat_full, rope_full, topk_d) for r in range(w.P)]
         for r, ri in enumerate(ranks):
@@ -387,11 +404,11 @@ class SparseRun:
         for r, ri in enumerate(ranks):
             if workspace:
                 args = pp.partial_args(pl, r, ri, self.ws, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                       topk=w.topk, window=w.window, kv_splits=kv_splits)
+                                       topk=w.topk, window=w.window, kv_splits=kv_splits, split_plan=split_plan)
             else:
                 args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
                                        kv_dtype=_lib.MLA_KV_FP8_E4M3, kv_scale=scale_d, topk=w.topk,
-                                       window=w.window, kv_splits=kv_splits)
+                                       window=w.window, kv_splits=kv_splits, split_plan=split_plan)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
@@ -490,10 +507,19 @@ def split_ranges(L, S):
     return [(64 * (s * n // S), 64 * ((s + 1) * n // S)) for s in range(S)]
 
 
+def row_split_counts(run, r):
+    """Key ranges of each virtual row of rank r: the split plan's (clamped into 1..S), else S."""
+    nv = run.plan.ranks[r].vrow_kv_len.shape[0]
+    if getattr(run, "split_plan", None) is None:
+        return np.full(nv, run.kv_splits)
+    return np.clip(run.split_plan.splits[r].cpu().numpy(), 1, run.kv_splits)
+
+
 def check_split_partials(run, tokens, key_rows, o_tol):
     """Every split slice of every rank's partial rows of the given tokens against the oracle
     restricted to that split's keys (no sink); a split with no key of the row must give
-    O = 0 and LSE = -inf. key_rows(t) -> (request-relative keys, latent fp64, rope fp64)."""
+    O = 0 and LSE = -inf, and a slice past the row's own range count (per-row split plan)
+    LSE = -inf. key_rows(t) -> (request-relative keys, latent fp64, rope fp64)."""
     w, plan, S = run.w, run.plan, run.kv_splits
     o_cat = on.bf16_to_f64(host_bits(run.bufs.o_cat))
     lse_cat = run.bufs.lse_cat.cpu().numpy()
@@ -501,12 +527,16 @@ def check_split_partials(run, tokens, key_rows, o_tol):
     tokset = set(int(t) for t in tokens)
     for r, rp in enumerate(plan.ranks):
         vrow = np.searchsorted(rp.cu_seqlens_q, np.arange(rp.T_loc), side="right") - 1
+        ns = row_split_counts(run, r)
         for i, g in enumerate(rp.local_gidx):
             g = int(g)
             if g not in tokset:
                 continue
             keys, lat, rope = key_rows(g)
-            for s, (lo, hi) in enumerate(split_ranges(int(rp.vrow_kv_len[vrow[i]]), S)):
+            n_v = int(ns[vrow[i]])
+            for s in range(n_v, S):  # slices the row does not use: LSE -inf (O unspecified)
+                assert np.all(np.isneginf(lse_cat[s * run.pl.T_total + plan.row_off[r] + i])), (g, s)
+            for s, (lo, hi) in enumerate(split_ranges(int(rp.vrow_kv_len[vrow[i]]), n_v)):
                 row = s * run.pl.T_total + plan.row_off[r] + i
                 sel = (keys >= lo) & (keys < hi)
                 if not sel.any():
@@ -552,6 +582,66 @@ def test_split_kv_dense(gpu_lib, seed):
         return keys, lat_all[rows], rope_all[rows]
     sample = hp.sample_tokens(w, run.plan, n_random=24)
     check_split_partials(run, sample, key_rows, O_TOL)
+
+
+def custom_split_plan(w, S, seed):
+    """Per-row key-range counts cycling through 1..S (shifted per rank, with a 0 and an S+3
+    among them, which the kernels clamp) and a random row order per rank."""
+    _, n_vrows, _ = _lib.pcp_plan_sizes(w.q_lens, w.kv_lens, w.P)
+    rng = np.random.default_rng(seed)
+    splits = np.array([[(v + r) % S + 1 for v in range(n_vrows)] for r in range(w.P)], np.int32)
+    splits[0, 0], splits[-1, -1] = 0, S + 3
+    order = np.stack([rng.permutation(n_vrows) for _ in range(w.P)]).astype(np.int32)
+    return pp.SplitPlan(S, torch.from_numpy(splits).cuda(), torch.from_numpy(order).cuda())
+
+
+SPLIT_PER_ROW = {
+    # seed: (q_lens, kv_lens, P, H, Dl, Dr, kv_splits)
+    321: ([700, 1, 130, 1, 5], [700, 3000, 900, 5000, 40], 2, 16, 512, 64, 4),  # prefill, decodes, continuations
+    322: ([300, 1, 9, 1], [300, 2000, 700, 100], 2, 4, 64, 16, 3),              # the 64+16 kernel
+    323: ([2048, 1, 1], [2048, 4000, 20], 4, 16, 512, 64, 8),                    # more ranges than short rows have
+}
+
+
+@pytest.mark.parametrize("seed", sorted(SPLIT_PER_ROW))
+def test_split_kv_dense_per_row(gpu_lib, seed):
+    """Per-row split KV on the dense kernels: every virtual row its own range count (1..S, out of
+    range counts clamped) in a random row order, partial buffers poisoned with NaN first. Every
+    used slice against the oracle on its range's keys, every unused slice LSE = -inf, and the
+    merge (which must not read the unused slices' outputs) against unsharded attention."""
+    q, kv, P, H, Dl, Dr, S = SPLIT_PER_ROW[seed]
+    w = synth.custom(seed, q, kv, P=P, H=H, Dl=Dl, Dr=Dr)
+    run = DenseRun(w, kv_splits=S, split_plan=custom_split_plan(w, S, seed))
+    check_plan(run.pl, run.plan)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    check_merged(run, ref, toks, O_TOL)
+    pos, req = hp.token_maps(run.plan)
+    lat_all, rope_all = on.bf16_to_f64(run.lat_bits), on.bf16_to_f64(run.rope_bits)
+
+    def key_rows(g):
+        keys = np.arange(int(pos[g]) + 1)
+        rows = int(w.kv_start[req[g]]) + keys
+        return keys, lat_all[rows], rope_all[rows]
+    check_split_partials(run, hp.sample_tokens(w, run.plan, n_random=48), key_rows, O_TOL)
+
+
+def test_split_plan_decode_heavy(gpu_lib):
+    """The library's split plan (pcp_plan_splits) on a decode-heavy batch -- 24 decode rows over
+    contexts of 2K-12K beside a short prefill, P=2 -- splits the decode rows; with NaN-poisoned
+    partial buffers the merged output of every token matches unsharded attention."""
+    rng = np.random.default_rng(331)
+    ctx = rng.integers(2048, 12288, size=24)
+    q = [256] + [1] * 24
+    kv = [256] + [int(c) for c in ctx]
+    w = synth.custom(331, q, kv, P=2, H=16, Dl=512, Dr=64)
+    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+    sp = pp.plan_splits(pl, w.H, w.Dl, max_splits=8)
+    assert sp.split_rows >= 2 * 24  # every decode row on both ranks
+    run = DenseRun(w, kv_splits=8, split_plan=sp)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    check_merged(run, ref, toks, O_TOL)
 
 
 def test_dense128k_p4_split_kv_sampled(gpu_lib):
@@ -610,6 +700,30 @@ def test_split_kv_sparse(gpu_lib):
         return keys, on.dequant_fp8_rows(run.lat_codes[rows], rows, run.kv_scale), on.bf16_to_f64(run.rope_bits[rows])
     sample = hp.sample_tokens(w, run.plan, n_random=24)
     check_split_partials(run, sample, key_rows, SPARSE_O_TOL)
+
+
+def test_split_kv_sparse_per_row(gpu_lib):
+    """Per-row split KV on both sparse paths: row range counts 1..3 (clamped) with NaN-poisoned
+    partials; used slices against the oracle on their keys, unused slices LSE = -inf, the
+    merge against unsharded sparse attention, and the two paths bit-identical."""
+    w = synth.custom(312, [900, 1, 400], [900, 2500, 1300], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,
+                     kv_dtype="fp8", latent_std=1.0)
+    sp = custom_split_plan(w, 3, 312)
+    run = SparseRun(w, kv_splits=3, split_plan=sp)
+    ws = SparseRun(w, kv_splits=3, split_plan=sp, workspace=True)
+    assert torch.equal(ws.bufs.o.view(torch.int16), run.bufs.o.view(torch.int16))
+    assert torch.equal(ws.bufs.lse, run.bufs.lse)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_sparse(w, run.plan, run.q_bits, run.lat_codes, run.kv_scale, run.rope_bits, run.topk,
+                           run.sink, toks)
+    check_merged(run, ref, toks, SPARSE_O_TOL)
+    pos, req = hp.token_maps(run.plan)
+
+    def key_rows(g):
+        keys = oa.sparse_keyset(int(pos[g]), run.topk[g], w.window)
+        rows = int(w.kv_start[req[g]]) + keys
+        return keys, on.dequant_fp8_rows(run.lat_codes[rows], rows, run.kv_scale), on.bf16_to_f64(run.rope_bits[rows])
+    check_split_partials(run, hp.sample_tokens(w, run.plan, n_random=24), key_rows, SPARSE_O_TOL)
 
 
 def test_dequant_workspace_bit_exact(gpu_lib):

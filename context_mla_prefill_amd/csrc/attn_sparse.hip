@@ -68,7 +68,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
     if (wk.split >= wk.nsplit) return;  // a range past the row's count: no keys, nothing to write
     const int tok = wk.tok;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in SGPRs
     const int pair = wave >> 1;
     const int side = wave & 1;
     const int lane = tid & 63;

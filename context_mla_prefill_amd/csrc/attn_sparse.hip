@@ -153,21 +153,29 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         }
     };
     // Dequantises staging slot b into the bf16 tile: thread handles 16-byte chunks tid,
-    // tid+256, ... (consecutive lanes read consecutive LDS bytes).
+    // tid+256, ... (consecutive lanes read consecutive LDS bytes). All of a thread's staged
+    // chunks and scales are read before any is converted, so their LDS latencies overlap.
     auto convert = [&](int b) {
+        constexpr int NCH = BN * DL / 16 / NT;
+        uint4 raw[NCH];
+        float sc[NCH];
 #pragma unroll
-        for (int i = 0; i < BN * DL / 16 / NT; ++i) {
+        for (int i = 0; i < NCH; ++i) {
+            const int k = i * NT + tid;
+            raw[i] = *reinterpret_cast<const uint4*>(stage[b] + k * 16);
+            sc[i] = stage_scale[b][k / (DL / 16)];
+        }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
             const int k = i * NT + tid;
             const int r = k / (DL / 16);
             const int c = k - r * (DL / 16);
-            const uint4 raw = *reinterpret_cast<const uint4*>(stage[b] + k * 16);
-            const float sc = stage_scale[b][r];
             bf16x8 o0, o1;
             __bf16 v[16];
-            dequant4(raw.x, sc, v);
-            dequant4(raw.y, sc, v + 4);
-            dequant4(raw.z, sc, v + 8);
-            dequant4(raw.w, sc, v + 12);
+            dequant4(raw[i].x, sc[i], v);
+            dequant4(raw[i].y, sc[i], v + 4);
+            dequant4(raw[i].z, sc[i], v + 8);
+            dequant4(raw[i].w, sc[i], v + 12);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 o0[e] = v[e];

@@ -87,3 +87,15 @@ def sample_tokens(w, plan, n_random=512, seed=None):
     if plan.T_glob:
         toks.update(int(x) for x in rng.integers(0, plan.T_glob, size=n_random))
     return np.array(sorted(toks), dtype=np.int64)
+
+
+def mixed_split_counts(w, S, seed):
+    """A per-row split plan for tests: key-range counts cycling through 1..S (shifted per rank,
+    with a 0 and an S+3 among them, which the kernels clamp) and a random row order per rank.
+    Returns int32 arrays [P][n_vrows] (counts, order)."""
+    n_vrows = oracle_plan(w).ranks[0].n_vrows
+    rng = np.random.default_rng(seed)
+    splits = np.array([[(v + r) % S + 1 for v in range(n_vrows)] for r in range(w.P)], np.int32)
+    splits[0, 0], splits[-1, -1] = 0, S + 3
+    order = np.stack([rng.permutation(n_vrows) for _ in range(w.P)]).astype(np.int32)
+    return splits, order

@@ -66,7 +66,7 @@ def check_paged_plan(pl, plan, bt):
 class DenseCacheRun:
     """partition -> bf16 insert -> P dense partials -> merge, on a packed or a paged cache."""
 
-    def __init__(self, w, seed=0, paged=True, kv_splits=1, table=None):
+    def __init__(self, w, seed=0, paged=True, kv_splits=1, table=None, split_plan=None):
         self.w, self.paged, self.kv_splits = w, paged, kv_splits
         self.plan = plan = hp.oracle_plan(w)
         print(f"[run] dense {'paged' if paged else 'packed'} {w.name} T={w.T_glob} kv_splits={kv_splits}",
@@ -106,7 +106,7 @@ class DenseCacheRun:
                                _lib.MLA_KV_BF16, N, self.kv_lat, self.kv_rope)
         for r, ri in enumerate(ranks):
             args = pp.partial_args(pl, r, ri, self.kv_lat, self.kv_rope, self.bufs, w.H, w.Dl, w.Dr, w.scale,
-                                   kv_splits=kv_splits)
+                                   kv_splits=kv_splits, split_plan=split_plan)
             _lib.mla_prefill_partial(args)
         pp.run_merge(pl, self.bufs, self.sink_d, w.H, w.Dl, kv_splits=kv_splits)
         torch.cuda.synchronize()
@@ -160,6 +160,23 @@ def test_paged_dense(gpu_lib, seed):
     packed = DenseCacheRun(w, paged=False, kv_splits=S)
     assert torch.equal(run.bufs.o_cat.view(torch.int16), packed.bufs.o_cat.view(torch.int16))
     assert torch.equal(run.bufs.lse_cat.view(torch.int32), packed.bufs.lse_cat.view(torch.int32))
+
+
+def test_paged_dense_per_row_split(gpu_lib):
+    """Paged cache with per-row split KV (row range counts 1..4, clamped, in a random row order):
+    the merge of every token against the oracle, and every partial slice bit-identical to the
+    packed run with the same plan (the unused slices' LSE = -inf on both)."""
+    w = synth.custom(404, [1500, 1, 200, 1], [1500, 2100, 333, 4100], P=2, H=16, Dl=512, Dr=64)
+    splits, order = hp.mixed_split_counts(w, 4, 404)
+    sp = pp.SplitPlan(4, torch.from_numpy(splits).cuda(), torch.from_numpy(order).cuda())
+    run = DenseCacheRun(w, seed=404, paged=True, kv_splits=4, split_plan=sp)
+    run.check_values()
+    packed = DenseCacheRun(w, paged=False, kv_splits=4, split_plan=sp)
+    lse_p, lse_k = run.bufs.lse_cat.cpu().numpy(), packed.bufs.lse_cat.cpu().numpy()
+    assert np.array_equal(lse_p.view(np.int32), lse_k.view(np.int32))
+    used = torch.from_numpy(np.isfinite(lse_p).all(axis=1)).cuda()  # slices a row's ranges wrote
+    assert torch.equal(run.bufs.o_cat[used].view(torch.int16), packed.bufs.o_cat[used].view(torch.int16))
+    assert np.isneginf(lse_p).any()  # some rows leave slices unused
 
 
 # ------------------------------------------------------------------ fp8 quantise-on-insert

@@ -585,13 +585,8 @@ def test_split_kv_dense(gpu_lib, seed):
 
 
 def custom_split_plan(w, S, seed):
-    """Per-row key-range counts cycling through 1..S (shifted per rank, with a 0 and an S+3
-    among them, which the kernels clamp) and a random row order per rank."""
-    _, n_vrows, _ = _lib.pcp_plan_sizes(w.q_lens, w.kv_lens, w.P)
-    rng = np.random.default_rng(seed)
-    splits = np.array([[(v + r) % S + 1 for v in range(n_vrows)] for r in range(w.P)], np.int32)
-    splits[0, 0], splits[-1, -1] = 0, S + 3
-    order = np.stack([rng.permutation(n_vrows) for _ in range(w.P)]).astype(np.int32)
+    """helpers.mixed_split_counts on the device."""
+    splits, order = hp.mixed_split_counts(w, S, seed)
     return pp.SplitPlan(S, torch.from_numpy(splits).cuda(), torch.from_numpy(order).cuda())
 
 
@@ -681,6 +676,50 @@ def test_dense128k_p4_split_kv_sampled(gpu_lib):
                 hp.compare(f"token {g} rank {r} split {s_}", o_row[None], lse_row[None], o0[None], lse0[None],
                            O_TOL, LSE_TOL)
     assert bool(torch.isfinite(run.bufs.o_cat.float()).all())
+
+
+def test_dense128k_p4_per_row_split_sampled(gpu_lib):
+    """The 128K P=4 workload under a per-row split plan (range counts 1..3 per virtual row,
+    clamped, rows in a random order) with NaN-poisoned partial buffers: on sampled tokens the
+    merge against unsharded attention, and for a subset every used slice against the oracle on
+    its keys and every unused slice LSE = -inf."""
+    w = synth.workload(3)
+    S = 3
+    run = DenseRun(w, kv_splits=S, split_plan=custom_split_plan(w, S, 333))
+    toks = np.asarray(sorted(set(int(t) for t in hp.sample_tokens(w, run.plan, n_random=512))))
+    print(f"[check] per-row split 128K: {len(toks)} sampled tokens", flush=True)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    sel_d = torch.from_numpy(toks).cuda()
+    hp.compare("128K merged over per-row splits", on.bf16_to_f64(host_bits(run.bufs.o.index_select(0, sel_d))),
+               run.bufs.lse.index_select(0, sel_d).cpu().numpy(), np.stack([ref[g][2] for g in toks]),
+               np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
+    pos, req = hp.token_maps(run.plan)
+    sub = set(int(t) for t in toks[::16])
+    for r, rp in enumerate(run.plan.ranks):
+        ns = row_split_counts(run, r)
+        vrow = np.searchsorted(rp.cu_seqlens_q, np.arange(rp.T_loc), side="right") - 1
+        for i in np.nonzero(np.isin(rp.local_gidx, list(sub)))[0]:
+            g = int(rp.local_gidx[i])
+            keys = np.arange(int(pos[g]) + 1)
+            base = int(w.kv_start[req[g]])
+            q = on.bf16_to_f64(run.q_bits[g])
+            n_v = int(ns[vrow[i]])
+            for s_ in range(S):
+                row = s_ * run.pl.T_total + run.plan.row_off[r] + int(i)
+                lse_row = run.bufs.lse_cat[row].cpu().numpy()
+                if s_ >= n_v:
+                    assert np.all(np.isneginf(lse_row)), (g, s_)
+                    continue
+                lo, hi = split_ranges(int(rp.vrow_kv_len[vrow[i]]), n_v)[s_]
+                o_row = on.bf16_to_f64(host_bits(run.bufs.o_cat[row]))
+                k = keys[(keys >= lo) & (keys < hi)]
+                if len(k) == 0:
+                    assert np.all(o_row == 0) and np.all(np.isneginf(lse_row)), (g, s_)
+                    continue
+                o0, lse0, _, _ = oa.attend_keyset(q, on.bf16_to_f64(run.lat_bits[base + k]),
+                                                  on.bf16_to_f64(run.rope_bits[base + k]), float(w.scale))
+                hp.compare(f"token {g} rank {r} split {s_}", o_row[None], lse_row[None], o0[None], lse0[None],
+                           O_TOL, LSE_TOL)
 
 
 def test_split_kv_sparse(gpu_lib):

@@ -76,8 +76,9 @@ def row_ranges(pl, splits: np.ndarray) -> np.ndarray:
     return out
 
 
-# sources the dense attention kernel is compiled from (its traffic record names their hash)
-ATTN_SOURCES = ("attn_dense.hip", "attn_dense_wide.hip", "attn_core.h", "work_order.h")
+# sources the benchmarked dense attention kernel (dense_wide_kernel) is compiled from; its
+# traffic record names their hash
+ATTN_SOURCES = ("attn_dense_wide.hip", "attn_core.h", "work_order.h")
 
 
 def measured_traffic(workload: int):

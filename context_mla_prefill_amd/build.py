@@ -22,8 +22,10 @@ SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense
            "attn_sparse.hip",
            "attn_sparse_bf16.hip", "topk_select.hip", "split_plan.hip"]
 
-# Per-file flags. The attention kernels keep O and the scores in VGPRs (MFMA VGPR form)
-# so its rare rescale is plain VALU work, leaving the AGPRs to Q.
+# Per-file flags. The attention kernels' builtin MFMAs accumulate in VGPRs (MFMA VGPR form):
+# the scores everywhere, and O in the 64-row kernels, whose rare rescale is then plain VALU
+# work while Q sits in AGPRs; the 512 + 64 dense kernel keeps O in AGPRs through inline-asm
+# P V MFMAs instead.
 EXTRA = {"attn_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_dense_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],

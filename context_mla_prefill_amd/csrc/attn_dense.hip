@@ -1,4 +1,6 @@
-// Rank-local causal MLA partial attention (dense), bf16 MFMA on gfx950.
+// Rank-local causal MLA partial attention (dense), bf16 MFMA on gfx950, for the small
+// 64 + 16 shape (latent 64, rope 16). The 512 + 64 shape runs the 128-row kernel of
+// attn_dense_wide.hip.
 //
 // Absorbed MLA is multi-query attention with one latent KV head: key = latent || rope,
 // value = latent. Every rank attends its local rows against the full all-gathered
@@ -14,10 +16,7 @@
 //    Q of those rows in registers for the whole KV loop.
 //  * KV tiles of BN = 64 keys move HBM -> LDS with direct-to-LDS loads into a double
 //    buffer (the next tile streams in while the current one is used) and are shared by
-//    all heads and waves. For the 512+64 shape the latent loads of the next tile are
-//    spread over the Q K^T MFMAs of the current one (two MFMAs apart), so the CU's
-//    vector memory pipe drains them while the matrix core runs instead of stalling the
-//    wave, and the barrier that publishes P orders LDS only, leaving them in flight.
+//    all heads and waves.
 //  * Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, A = K from
 //    LDS, B = Q^T from registers); wave s of a pair scores keys [32 s, 32 s + 32) of the
 //    tile. Each lane then holds scores of ONE query row, so the row max needs one
@@ -42,82 +41,37 @@ namespace {
 
 using namespace attn;
 
-// LDS image of one KV tile of the dense kernel.
-//  * Latent rows at a stride of DL*2 + 16 bytes; inside every block of 16 keys, key
-//    (score row) r sits in LDS row kperm(r) (conflict-free Q K^T and V^T reads).
-//  * 512+64 ("wide"): one latent row per direct-to-LDS load, so the source row of a
-//    load is wave-uniform and its address scalar. Rope rows are packed 8 per load at
-//    128 bytes with no pad; the 16-byte chunk c of row r is stored at chunk
-//    c ^ ((r / 2) % 8), which keeps the Q K^T rope reads conflict-free.
-//  * Other shapes: several latent rows per load, rope rows at a stride of DR*2 + 16,
-//    loads predicated per lane (no interleaving).
+// LDS image of one KV tile of the dense kernel: latent rows at a stride of DL*2 + 16
+// bytes (inside every block of 16 keys, key (score row) r sits in LDS row kperm(r):
+// conflict-free Q K^T and V^T reads), rope rows after them at a stride of DR*2 + 16;
+// several rows per direct-to-LDS load, loads predicated per lane.
 template <int DL, int DR>
 struct DenseTile {
-    static constexpr bool WIDE = DL * 2 == 1024 && DR * 2 == 128;
     static constexpr int DQK = DL + DR;
     static constexpr int KB = DQK / 16;  // 16-wide k-blocks of Q K^T
     static constexpr int NB = DL / 32;   // 32-wide column blocks of O
     static constexpr int LAT_VECS = DL / 8;
     static constexpr int ROPE_VECS = DR / 8;
     static constexpr int LAT_STRIDE = DL * 2 + 16;
-    static constexpr int ROPE_STRIDE = WIDE ? DR * 2 : DR * 2 + 16;
+    static constexpr int ROPE_STRIDE = DR * 2 + 16;
     static constexpr int ROPE_OFF = BN * LAT_STRIDE;
     static constexpr int TILE_BYTES = ROPE_OFF + BN * ROPE_STRIDE;
-    static constexpr int LAT_ROWS_PER_LOAD = WIDE ? 1 : 64 / (LAT_VECS + 1);
-    static constexpr int ROPE_ROWS_PER_LOAD = WIDE ? 8 : 64 / (ROPE_VECS + 1);
+    static constexpr int LAT_ROWS_PER_LOAD = 64 / (LAT_VECS + 1);
+    static constexpr int ROPE_ROWS_PER_LOAD = 64 / (ROPE_VECS + 1);
     static constexpr int LAT_LOADS = (BN + LAT_ROWS_PER_LOAD - 1) / LAT_ROWS_PER_LOAD;
     static constexpr int ROPE_LOADS = (BN + ROPE_ROWS_PER_LOAD - 1) / ROPE_ROWS_PER_LOAD;
-    // wide shape: every wave issues LAT_PER_WAVE latent loads of the next tile, one after
-    // every LOAD_GAP-th Q K^T MFMA (the last few, which find no slot there, go among the
-    // final MFMAs of the chain), and its ROPE_PER_WAVE rope loads right after the chain
-    static constexpr int LAT_PER_WAVE = LAT_LOADS / 4;    // 16
-    static constexpr int ROPE_PER_WAVE = ROPE_LOADS / 4;  // 2
-    static constexpr int LOAD_GAP = 2;
     static_assert(DQK % 16 == 0 && DL % 32 == 0 && DR % 8 == 0, "tile shape");
-    static_assert(!WIDE || (LAT_LOADS % 4 == 0 && ROPE_LOADS % 4 == 0), "wide loads split evenly over 4 waves");
+    static_assert(LAT_ROWS_PER_LOAD >= 1 && DL * 2 < 1024, "several latent rows per load (the small shape)");
 };
 
-// Wide shape: buffer views of the rows of KV tile kt. The base is the tile's first row,
-// clamped to the last valid row (the loads issued after the final tile read that row into
-// the unused buffer); the range is the valid rows from the base, so a load can only touch
-// rows of this request's extent. Buffer loads rather than global ones: the compiler counts
-// a global (flat-family) load into LDS as an LDS access of unknown order and would then
-// wait for all LDS reads at once instead of keeping the Q K^T reads in flight.
 // Where the keys of one tile live: KV row of its first key and how many keys it has.
 struct TileRows {
     int64_t row0;
     int rows;  // 1..BN
 };
 
-template <class T, int DL, int DR>
-struct WideTile {
-    __amdgpu_buffer_rsrc_t lat_rsrc, rope_rsrc;
-    int rows;  // valid rows from the base, 1..BN
-    __device__ __forceinline__ WideTile(const char* lat, const char* rope, TileRows tr) : rows(tr.rows) {
-        lat_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(lat + tr.row0 * (DL * 2)), 0, rows * (DL * 2), kBufferFlags);
-        rope_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rope + tr.row0 * (DR * 2)), 0, rows * (DR * 2), kBufferFlags);
-    }
-    // Latent load i (0..15) of this wave: tile row n = 4 i + wave, one 1024-byte row per
-    // load (row offset in an SGPR, lane offset constant). Rows past the extent repeat the
-    // last valid row (finite values; their scores are masked).
-    __device__ __forceinline__ void lat_load(char* dst, int wave, int lane, int i) const {
-        const int n = i * 4 + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(dst + n * T::LAT_STRIDE), 16, lane * 16,
-                                                 min(n, rows - 1) * (DL * 2), 0, 0);
-    }
-    // Rope load u (0..1) of this wave: rows 8 n .. 8 n + 7 with n = 2 wave + u. Lane l fills
-    // LDS chunk l % 8 of row 8 n + l / 8, i.e. source chunk (l % 8) ^ ((row / 2) % 8).
-    __device__ __forceinline__ void rope_load(char* dst, int wave, int lane, int u) const {
-        const int n = 2 * wave + u;
-        const int r = n * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rsrc, (lds_void*)(dst + T::ROPE_OFF + n * 1024), 16,
-                                                 min(r, rows - 1) * (DR * 2) + c * 16, 0, 0, 0);
-    }
-};
-
-// Other shapes: every load of a tile, lanes that would land on a pad switched off. Keys
-// past the tile's extent repeat its last key. Wave w issues loads w, w+4, ...
+// Every load of a tile, lanes that would land on a pad switched off. Keys past the tile's
+// extent repeat its last key. Wave w issues loads w, w+4, ...
 template <class T, int DL, int DR>
 __device__ __forceinline__ void narrow_load_tile(char* dst, const char* __restrict__ lat,
                                                  const char* __restrict__ rope, TileRows tr, int wave, int lane) {
@@ -272,12 +226,8 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     const int k_lat_off = krow * T::LAT_STRIDE + 16 * half;
     int k_rope_off[T::KB - DL / 16];
 #pragma unroll
-    for (int kb = 0; kb < T::KB - DL / 16; ++kb) {
-        if constexpr (T::WIDE)
-            k_rope_off[kb] = T::ROPE_OFF + krow * T::ROPE_STRIDE + 16 * ((2 * kb + half) ^ ((krow >> 1) & 7));
-        else
-            k_rope_off[kb] = T::ROPE_OFF + krow * T::ROPE_STRIDE + 16 * half + 32 * kb;
-    }
+    for (int kb = 0; kb < T::KB - DL / 16; ++kb)
+        k_rope_off[kb] = T::ROPE_OFF + krow * T::ROPE_STRIDE + 16 * half + 32 * kb;
     const int v_off = kperm(4 * half + ((lane & 15) >> 2)) * T::LAT_STRIDE + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
     const int n_tiles = (kv_hi + BN - 1) / BN;
@@ -285,52 +235,34 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
     // One KV tile: wait for it, publish it, then scores, softmax, P exchange and P V on
     // it while the next tile streams into the other buffer. The two buffers are distinct
     // LDS objects, so the compiler can tell that the streaming loads never touch the tile
-    // being read and does not wait for them. The wide shape issues the next tile's loads
-    // unconditionally (clamped rows; after the last tile they refill an unused buffer).
+    // being read and does not wait for them.
     auto tile_step = [&](const char* kvt, char* nxt, int kt) {
 #pragma unroll
         for (int kb = 0; kb < T::KB; ++kb) asm volatile("" : "+a"(qf[kb]));  // Q stays in AGPRs
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
         __syncthreads();                     // ... and every wave's; the other buffer is free
-        const TileRows next_rows = tile_rows(kt + 1);  // clamped past the last tile
-        if constexpr (!T::WIDE) {
-            if (kt + 1 < n_tiles) narrow_load_tile<T, DL, DR>(nxt, lat, rope, next_rows, wave, lane);
-        }
+        if (kt + 1 < n_tiles) narrow_load_tile<T, DL, DR>(nxt, lat, rope, tile_rows(kt + 1), wave, lane);
         // S^T[key, row] for keys 32*side + 8*(i/4) + 4*half + i%4 of this tile, row l32.
         f32x16 s = f32x16{};
         {
             const char* kl = kvt + k_lat_off;
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (T::WIDE) {
-                const WideTile<T, DL, DR> src(lat, rope, next_rows);
-#pragma unroll
-                for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(nxt, wave, lane, i);
-            }
 #pragma unroll
             for (int kb = 0; kb < T::KB; ++kb) {
                 const char* ap = kb < DL / 16 ? kl + kb * 32 : kvt + k_rope_off[kb - DL / 16];
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], s, 0, 0, 0);
             }
-            // QK_AHEAD operand reads in flight ahead of the MFMA chain; a load of the next
-            // tile after every LOAD_GAP-th MFMA, so the vector memory pipe drains them
-            // while the matrix core runs instead of stalling the wave on a burst.
+            // QK_AHEAD operand reads in flight ahead of the MFMA chain.
             constexpr int AHEAD = T::KB < QK_AHEAD ? T::KB : QK_AHEAD;
             __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
             for (int kb = 0; kb < T::KB - AHEAD; ++kb) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (T::WIDE && kb % T::LOAD_GAP == 0 && kb / T::LOAD_GAP < T::LAT_PER_WAVE)
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
             __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (T::WIDE) {
-            const WideTile<T, DL, DR> src(lat, rope, next_rows);
-#pragma unroll
-            for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(nxt, wave, lane, u);
         }
         // V^T operands of the first P V MFMAs (key-block-major: kb = m / NB0, d = m % NB0):
         // they do not depend on P, so their LDS reads run under the softmax.
@@ -432,16 +364,7 @@ __global__ __launch_bounds__(NT, 1) void dense_partial_kernel(
 
     if (kt0 < n_tiles) {  // workgroup-uniform; an empty key range leaves O = 0, LSE = -inf
         if constexpr (PAGED) bw_load(min(kt0, nblk - 1) & ~63);
-        const TileRows first_rows = tile_rows(kt0);
-        if constexpr (T::WIDE) {
-            const WideTile<T, DL, DR> src(lat, rope, first_rows);
-#pragma unroll
-            for (int i = 0; i < T::LAT_PER_WAVE; ++i) src.lat_load(kv_lds0, wave, lane, i);
-#pragma unroll
-            for (int u = 0; u < T::ROPE_PER_WAVE; ++u) src.rope_load(kv_lds0, wave, lane, u);
-        } else {
-            narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, first_rows, wave, lane);
-        }
+        narrow_load_tile<T, DL, DR>(kv_lds0, lat, rope, tile_rows(kt0), wave, lane);
         for (int kt = kt0; kt < n_tiles; kt += 2) {
             tile_step(kv_lds0, kv_lds1, kt);
             if (kt + 1 >= n_tiles) break;
@@ -491,12 +414,7 @@ hipError_t launch_dense(const mla_partial_args& a, hipStream_t stream) {
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream) {
     if (a.D_latent == 512) return launch_dense_wide_partial(a, stream);  // 128-row workgroups
-    if (a.block_table) {
-        if (a.D_latent == 512) return launch_dense<512, 64, true>(a, stream);
-        return launch_dense<64, 16, true>(a, stream);
-    }
-    if (a.D_latent == 512) return launch_dense<512, 64, false>(a, stream);
-    return launch_dense<64, 16, false>(a, stream);
+    return a.block_table ? launch_dense<64, 16, true>(a, stream) : launch_dense<64, 16, false>(a, stream);
 }
 
 }  // namespace mla

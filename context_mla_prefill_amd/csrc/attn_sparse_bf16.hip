@@ -42,7 +42,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
         sparse_work(H, kv_splits, cu, n_vrows, vrow_kv_start, positions, vrow_kv_len, vrow_splits);
     if (wk.split >= wk.nsplit) return;  // a range past the row's count: no keys, nothing to write
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it in SGPRs
+    // wave-uniform; read into an SGPR for packed KV only (paged: measured 9 % slower that way)
+    const int wave = PAGED ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1;
     const int side = wave & 1;
     const int lane = tid & 63;

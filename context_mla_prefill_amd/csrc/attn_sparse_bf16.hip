@@ -66,14 +66,15 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rope + row_base * (DR * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DR * 2)), kBufferFlags);
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[wk.lo_v] * bt_stride : nullptr;
-    const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row, bt_stride);
-
+    // Q rows first: their loads are in flight while the selected-row list is built
     bf16x8 qf[S::KB];
     {
         const __bf16* qrow = q + grow * S::DQK + 8 * half;
 #pragma unroll
         for (int kb = 0; kb < S::KB; ++kb) qf[kb] = valid ? *reinterpret_cast<const bf16x8*>(qrow + kb * 16) : bf16x8{};
     }
+    const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row, bt_stride);
+
     __syncthreads();
 
     const int n_tiles = ks.n_tiles;

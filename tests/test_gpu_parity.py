@@ -639,6 +639,22 @@ def test_split_plan_decode_heavy(gpu_lib):
     check_merged(run, ref, toks, O_TOL)
 
 
+def test_split_plan_at_most_64_ranges(gpu_lib):
+    """The largest split count (64 ranges, P = 1, the merge's limit P * kv_splits = 64): the
+    planner's plan for four decode rows over 3K-100K keys, poisoned partial buffers, every
+    token's merge against unsharded attention."""
+    w = synth.custom(332, [1, 1, 1, 1], [100000, 70000, 50000, 3000], P=1, H=16, Dl=512, Dr=64)
+    pl = pp.alloc_plan(w.q_lens, w.kv_lens, w.kv_start, w.P)
+    sp = pp.plan_splits(pl, w.H, w.Dl, max_splits=64)
+    counts = sp.splits.cpu().numpy()
+    print(f"[check] plan ranges {counts.tolist()}", flush=True)
+    assert counts.max() > 8  # long rows cut into many ranges
+    run = DenseRun(w, kv_splits=64, split_plan=sp)
+    toks = np.arange(w.T_glob)
+    ref = hp.oracle_dense(w, run.plan, run.q_bits, run.lat_bits, run.rope_bits, run.sink, toks)
+    check_merged(run, ref, toks, O_TOL)
+
+
 def test_dense128k_p4_split_kv_sampled(gpu_lib):
     """The 128K P=4 workload with each virtual row's keys cut into two ranges (the launch
     bench.py --kv-splits 2 times): on sampled tokens, the merge of all eight (rank, split)

@@ -37,6 +37,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     __shared__ int sel[MAX_TOPK];
     __shared__ int win_blk[MAX_WINDOW / BN + 1];
     __shared__ Exchange ex;
+    static_assert(S::DQK == 8 * Q_CHUNKS && S::ROPE_OFF >= Q_REGION_BYTES, "Q rows of a wave pair fit a tile buffer");
 
     const SparseWork wk =
         sparse_work(H, kv_splits, cu, n_vrows, vrow_kv_start, positions, vrow_kv_len, vrow_splits);
@@ -66,16 +67,18 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rope + row_base * (DR * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DR * 2)), kBufferFlags);
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[wk.lo_v] * bt_stride : nullptr;
-    // Q rows first: their loads are in flight while the selected-row list is built
-    bf16x8 qf[S::KB];
-    {
-        const __bf16* qrow = q + grow * S::DQK + 8 * half;
-#pragma unroll
-        for (int kb = 0; kb < S::KB; ++kb) qf[kb] = valid ? *reinterpret_cast<const bf16x8*>(qrow + kb * 16) : bf16x8{};
-    }
+    // Q rows first, into the latent buffers (pair 0 into the first, pair 1 into the second):
+    // their loads are in flight while the selected-row list is built
+    char* const q_region = pair == 0 ? kv_lat0 : kv_lat1;
+    dma_q_rows(__builtin_amdgcn_make_buffer_rsrc((void*)(q + (int64_t)wk.tok * H * S::DQK), 0, H * S::DQK * 2,
+                                                 kBufferFlags),
+               wk.hg * BM + pair * 32, H, q_region, side, lane);
     const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row, bt_stride);
 
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's Q rows landed
+    __syncthreads();                     // ... every wave's, and the selected-row list is written
+    bf16x8 qf[S::KB];
+    read_q_frags(q_region, lane, qf);
 
     const int n_tiles = ks.n_tiles;
     // Latent rows of tile t into buffer dst: wave w loads slots 16w .. 16w+15, one row each;
@@ -120,6 +123,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
 
     int t = ks.next_live(0, lane);
     int tn = n_tiles;
+    lds_barrier();  // every wave holds its Q fragments: the first tile may overwrite pair 0's rows
     if (t < n_tiles) {
         const int row = lat_rows(t);
 #pragma unroll

@@ -60,6 +60,43 @@ __device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const in
     return w;
 }
 
+// Q rows of a workgroup through LDS. A token's Q rows are contiguous (H rows of 1152 bytes),
+// so direct-to-LDS loads move them in whole cache lines, where per-lane fragment loads would
+// touch 32 bytes of a row per instruction. Wave pair p copies its 32 rows into `region` (36 KB
+// of a tile buffer not yet in use), each of its two waves 18 loads of 64 x 16 bytes. 16-byte
+// chunk c of row r goes to chunk r * 72 + (c ^ f(r)), f(r) = (r ^ (r >> 3)) % 8: the fragment
+// reads (row r = lane % 32, one chunk per lane) then meet distinct bank slots both for 8
+// consecutive lanes over 128 bytes and for 16 over 256. Rows past the head count read row H - 1
+// (their results are never stored).
+constexpr int Q_CHUNKS = 72;                      // 16-byte chunks of a 576-element bf16 row
+constexpr int Q_REGION_BYTES = 32 * Q_CHUNKS * 16;  // one wave pair's rows
+__device__ __forceinline__ int q_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
+// q_rsrc: the token's Q rows; row0: head of the pair's first row.
+__device__ __forceinline__ void dma_q_rows(__amdgpu_buffer_rsrc_t q_rsrc, int row0, int H, char* region, int side,
+                                           int lane) {
+    static_assert(NT / 64 == 4, "two waves per pair");
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+        const int i = 2 * j + side;  // load i of the pair fills LDS chunks 64 i .. 64 i + 63
+        const int L = 64 * i + lane;
+        const int r = L / Q_CHUNKS;
+        const int c = (L - r * Q_CHUNKS) ^ q_swizzle(r);
+        const int row = min(row0 + r, H - 1);
+        lds_dma16(q_rsrc, (uint32_t)(row * (Q_CHUNKS * 16) + c * 16), region + 1024 * i);
+    }
+}
+// Q K^T operand fragments of row lane % 32 of the pair from `region`: elements
+// [16 kb + 8 (lane / 32), +8) of the row.
+template <int KB>
+__device__ __forceinline__ void read_q_frags(const char* region, int lane, bf16x8 (&qf)[KB]) {
+    const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int c = (2 * kb + half) ^ q_swizzle(r);
+        qf[kb] = *reinterpret_cast<const bf16x8*>(region + 16 * (r * Q_CHUNKS + c));
+    }
+}
+
 // Rows of the keys: relative to the request's first row for packed KV (row = key position),
 // absolute for paged KV (row = block_table entry * 64 + position % 64).
 template <bool PAGED>

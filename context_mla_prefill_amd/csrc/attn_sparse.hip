@@ -233,7 +233,7 @@ __global__ __launch_bounds__(NT, 1) void sparse_partial_kernel(
         b ^= 1;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the unused last gather landed before LDS is released
-    write_rows<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, o_out, lse_out);
+    write_rows_staged<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, kv_lat, o_out, lse_out);
     sched::mark_empty_slices(lse0, grow, valid && side == 0 && half == 0, wk.split, wk.nsplit, kv_splits,
                              split_stride, H);
 }

@@ -159,8 +159,8 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
         if (t >= n_tiles) break;
         step(kv_lat1, kv_lat0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    write_rows<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, o_out, lse_out);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the pad rows past the last tile landed before LDS is reused
+    write_rows_staged<S, DL>(acc_o, m_ref, l_run, valid, grow, wave, side, lane, ex, kv_lat0, o_out, lse_out);
     sched::mark_empty_slices(lse0, grow, valid && side == 0 && half == 0, wk.split, wk.nsplit, kv_splits,
                              split_stride, H);
 }

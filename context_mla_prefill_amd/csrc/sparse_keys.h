@@ -97,6 +97,63 @@ __device__ __forceinline__ void read_q_frags(const char* region, int lane, bf16x
     }
 }
 
+// Epilogue of a sparse workgroup: the normalised O rows go through LDS so that every global
+// store writes one whole 1 KB row (the MFMA layout leaves a lane 8 bytes of each of 32 rows per
+// store otherwise); LSE as in the dense epilogue. `region` is a free 64 KB tile buffer (the
+// caller has waited for its own loads into LDS). 8-byte chunk q of row r sits at chunk
+// q ^ (r % 32), so the row-per-lane writes (32 rows at one chunk) meet distinct bank slots for
+// both 16 lanes over 128 bytes and 32 over 256, and each row stays inside its own 1 KB.
+// grow: this lane's global row; valid: it is below the head count (the valid rows of a
+// workgroup are a prefix). The workgroup's first row and valid-row count are derived here from
+// these two, so nothing more stays live through the key loop.
+template <class S, int DL>
+__device__ __forceinline__ void write_rows_staged(const f32x16 (&acc_o)[S::NB / 2], float m_ref, float l_run,
+                                                  bool valid, int64_t grow, int wave, int side, int lane,
+                                                  Exchange& ex, char* region, __bf16* __restrict__ o_out,
+                                                  float* __restrict__ lse_out) {
+    static_assert(DL * 2 == 1024 && BM * DL * 2 <= S::ROPE_OFF, "64 rows of 1 KB fit a tile buffer");
+    constexpr int NB0 = S::NB / 2;
+    const int half = lane >> 5;
+    const int r = (wave >> 1) * 32 + (lane & 31);  // this lane's row of the workgroup
+    const float l_w = l_run + __shfl_xor(l_run, 32);
+    const int n_mine = __popcll(__ballot(valid)) / 2;  // valid rows of this wave's pair
+    __syncthreads();  // every wave is past its last tile: the tile buffers are free
+    ex.mx[wave][lane] = l_w;
+    if (lane == 0) ex.flag[wave] = n_mine;
+    __syncthreads();
+    const float l_tot = l_w + ex.mx[wave ^ 1][lane];
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int n_valid = __builtin_amdgcn_readfirstlane(n_mine + ex.flag[wave ^ 2]);
+    char* const lrow = region + r * (DL * 2);
+#pragma unroll
+    for (int d = 0; d < NB0; ++d) {
+        const int db = side * NB0 + d;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (__bf16)(acc_o[d][4 * g + e] * inv);
+            const int q = (db * 32 + 8 * g + 4 * half) / 4;
+            *reinterpret_cast<bf16x4*>(lrow + 8 * (q ^ (r & 31))) = y;
+        }
+    }
+    if (valid && side == 0 && half == 0) lse_out[grow] = (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    __syncthreads();
+    // wave w stores rows 16w .. 16w+15; lane l the row's bytes [16 l, 16 l + 16): stored chunks
+    // 2l ^ s and 2l+1 ^ s (s = row % 32) share the 16-byte slot l ^ (s / 2), swapped when s is odd
+    __bf16* const o_wg = o_out + (grow - r) * DL + 8 * lane;  // the workgroup's first row
+    constexpr int ROWS = BM / (NT / 64);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int row = ROWS * wave + i;
+        if (row >= n_valid) break;  // wave-uniform
+        const int s = row & 31;
+        uint4 v = *reinterpret_cast<const uint4*>(region + row * (DL * 2) + 16 * (lane ^ (s >> 1)));
+        if (s & 1) v = uint4{v.z, v.w, v.x, v.y};
+        *reinterpret_cast<uint4*>(o_wg + row * DL) = v;
+    }
+}
+
 // Rows of the keys: relative to the request's first row for packed KV (row = key position),
 // absolute for paged KV (row = block_table entry * 64 + position % 64).
 template <bool PAGED>

@@ -229,7 +229,7 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: q/KV/output must be 16-byte aligned");
     hipError_t e = !sparse ? launch_dense_partial(*a, (hipStream_t)stream)
                    : a->kv_dtype == MLA_KV_FP8_E4M3 ? launch_sparse_partial(*a, (hipStream_t)stream)
-                                                    : launch_sparse_bf16_partial(*a, (hipStream_t)stream);
+                                                    : launch_sparse_wide_partial(*a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_prefill_partial: %s", hipGetErrorString(e));
     return MLA_OK;
 }

@@ -70,9 +70,9 @@ __global__ __launch_bounds__(NT, 1) void sparse_bf16_partial_kernel(
     // Q rows first, into the latent buffers (pair 0 into the first, pair 1 into the second):
     // their loads are in flight while the selected-row list is built
     char* const q_region = pair == 0 ? kv_lat0 : kv_lat1;
-    dma_q_rows(__builtin_amdgcn_make_buffer_rsrc((void*)(q + (int64_t)wk.tok * H * S::DQK), 0, H * S::DQK * 2,
-                                                 kBufferFlags),
-               wk.hg * BM + pair * 32, H, q_region, side, lane);
+    dma_q_rows<2>(__builtin_amdgcn_make_buffer_rsrc((void*)(q + (int64_t)wk.tok * H * S::DQK), 0, H * S::DQK * 2,
+                                                    kBufferFlags),
+                  wk.hg * BM + pair * 32, H, q_region, side, lane);
     const SparseKeys<PAGED> ks = sparse_keys<PAGED>(sel, win_blk, topk_idx, topk, window, wk, bt_row, bt_stride);
 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's Q rows landed

@@ -62,22 +62,23 @@ __device__ __forceinline__ SparseWork sparse_work(int H, int kv_splits, const in
 
 // Q rows of a workgroup through LDS. A token's Q rows are contiguous (H rows of 1152 bytes),
 // so direct-to-LDS loads move them in whole cache lines, where per-lane fragment loads would
-// touch 32 bytes of a row per instruction. Wave pair p copies its 32 rows into `region` (36 KB
-// of a tile buffer not yet in use), each of its two waves 18 loads of 64 x 16 bytes. 16-byte
-// chunk c of row r goes to chunk r * 72 + (c ^ f(r)), f(r) = (r ^ (r >> 3)) % 8: the fragment
-// reads (row r = lane % 32, one chunk per lane) then meet distinct bank slots both for 8
-// consecutive lanes over 128 bytes and for 16 over 256. Rows past the head count read row H - 1
-// (their results are never stored).
+// touch 32 bytes of a row per instruction. The WAVES waves that share 32 rows copy them into
+// `region` (36 KB of a tile buffer not yet in use) with 36 loads of 64 x 16 bytes between them,
+// wave `first` taking loads first, first + WAVES, ... 16-byte chunk c of row r goes to chunk
+// r * 72 + (c ^ f(r)), f(r) = (r ^ (r >> 3)) % 8: the fragment reads (row r = lane % 32, one
+// chunk per lane) then meet distinct bank slots both for 8 consecutive lanes over 128 bytes and
+// for 16 over 256. Rows past the head count read row H - 1 (their results are never stored).
 constexpr int Q_CHUNKS = 72;                      // 16-byte chunks of a 576-element bf16 row
-constexpr int Q_REGION_BYTES = 32 * Q_CHUNKS * 16;  // one wave pair's rows
+constexpr int Q_REGION_BYTES = 32 * Q_CHUNKS * 16;  // 32 rows
 __device__ __forceinline__ int q_swizzle(int r) { return (r ^ (r >> 3)) & 7; }
-// q_rsrc: the token's Q rows; row0: head of the pair's first row.
-__device__ __forceinline__ void dma_q_rows(__amdgpu_buffer_rsrc_t q_rsrc, int row0, int H, char* region, int side,
+// q_rsrc: the token's Q rows; row0: head of the first of the 32 rows.
+template <int WAVES>
+__device__ __forceinline__ void dma_q_rows(__amdgpu_buffer_rsrc_t q_rsrc, int row0, int H, char* region, int first,
                                            int lane) {
-    static_assert(NT / 64 == 4, "two waves per pair");
+    static_assert(Q_CHUNKS * 32 % (64 * WAVES) == 0, "loads split evenly over the waves");
 #pragma unroll
-    for (int j = 0; j < 18; ++j) {
-        const int i = 2 * j + side;  // load i of the pair fills LDS chunks 64 i .. 64 i + 63
+    for (int j = 0; j < Q_CHUNKS * 32 / 64 / WAVES; ++j) {
+        const int i = WAVES * j + first;  // load i fills LDS chunks 64 i .. 64 i + 63
         const int L = 64 * i + lane;
         const int r = L / Q_CHUNKS;
         const int c = (L - r * Q_CHUNKS) ^ q_swizzle(r);

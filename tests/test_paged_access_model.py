@@ -13,7 +13,8 @@ the size of the buffer it touches:
 * the paged dense kernel's 64-tile window of block ids, its tile rows and the latent and
   rope loads (including the loads issued after a row's last tile);
 * the sparse key sets (selected rows through the table, window blocks, the pad row) and the
-  row clamps, latent / rope / scale offsets of both sparse kernels;
+  row clamps, latent / rope / scale offsets of the sparse kernels (the bf16 kernel reads the
+  table only at the blocks of keys of the set and of key 0, a subset of what is modelled);
 * the merge's contributor rows.
 
 It also shows the cause of the fault that test met: built on an fp8 workload, the sparse
@@ -159,7 +160,7 @@ def model_dense_paged(bufs, w, rp, bt, N_kv):
 
 
 def model_sparse(bufs, w, rp, bt, N_kv, topk_rows, row_bytes):
-    """Both sparse kernels of one rank (one workgroup per token and 64 heads): the selected
+    """The sparse kernels of one rank (one workgroup per token and 64 heads): the selected
     index row, the table reads of sparse_keys (clamped columns; the pad row is block 0's first
     row; the window's blocks), every key row clamped into [0, N_kv - 1] before an offset is
     formed, and the latent (row_bytes per row), rope and scale reads of those rows. Returns

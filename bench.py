@@ -78,7 +78,7 @@ def row_ranges(pl, splits: np.ndarray) -> np.ndarray:
 
 # sources the benchmarked dense attention kernel (dense_wide_kernel) is compiled from; its
 # traffic record names their hash
-ATTN_SOURCES = ("attn_dense_wide.hip", "attn_core.h", "work_order.h")
+ATTN_SOURCES = ("attn_dense_wide.hip", "attn_core.h", "wide_tile.h", "work_order.h")
 
 
 def measured_traffic(workload: int):

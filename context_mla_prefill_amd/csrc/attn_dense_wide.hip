@@ -39,12 +39,20 @@
 #include <type_traits>
 
 #include "attn_core.h"
+#include "wide_tile.h"
 #include "work_order.h"
 
 namespace mla {
 namespace {
 
 using namespace attn;
+using wide::kRefSlack;
+using wide::NBO;
+using wide::o_read_fence;
+using wide::o_zero;
+using wide::p_fence;
+using wide::pv_mfma;
+using wide::Softmax;
 
 constexpr int WBM = 128;   // rows per workgroup
 constexpr int TK = 32;     // keys per KV tile
@@ -52,14 +60,13 @@ constexpr int DL = 512, DR = 64;
 constexpr int DQK = DL + DR;
 constexpr int KB = DQK / 16;             // 36 k-blocks of Q K^T
 constexpr int KBL = DL / 16;             // 32 of them latent
-constexpr int NBO = DL / 32;             // 16 output column blocks of 32
 constexpr int LAT_STRIDE = DL * 2 + 16;  // 1040: an odd number of 16-byte bank slots
 constexpr int ROPE_OFF = TK * LAT_STRIDE;
 constexpr int TILE_BYTES = ROPE_OFF + TK * DR * 2;
 constexpr int LAT_PER_WAVE = TK / 4;  // 8 latent row loads per wave and tile
 constexpr int QK_AHEAD = 4;           // Q K^T operand reads in flight
 constexpr int PV_AHEAD_W = 2;         // P V MFMAs' worth of V^T reads in flight
-constexpr float kRefSlack = 32.0f;    // log2 headroom of the fixed reference
+static_assert(NBO == DL / 32, "16 output column blocks of 32");
 
 // Where the keys of one tile live: KV row of its first key and how many keys it has.
 struct TileRows {
@@ -95,33 +102,6 @@ struct TileSrc {
     }
 };
 
-// O lives in AGPRs and is written by P V MFMAs issued as inline asm, which the compiler's
-// hazard tracking does not see as MFMAs. The epilogue, the one place where ordinary
-// instructions read O, first waits out the last MFMA's write latency; the asm statement takes
-// O as operands so it stays ordered after the MFMAs.
-#define MLA_O_OPERANDS(o)                                                                                   \
-    "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]),         \
-        "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]), "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15])
-__device__ __forceinline__ void o_read_fence(f32x16 (&o)[NBO]) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O_OPERANDS(o));
-}
-
-// Zeroes an O block where it lives (an MFMA of zero operands with a zero accumulator writes
-// zeros to its 16 AGPRs), so every value of O is defined in AGPRs and the compiler never moves
-// O through VGPRs.
-__device__ __forceinline__ void o_zero(f32x16& o) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(o) : "v"(bf16x8{}));
-}
-
-// P is written by VALU instructions and read by the P V MFMAs issued as asm, whose operands
-// the compiler's hazard tracking does not see: two wait states between them.
-__device__ __forceinline__ void p_fence(bf16x8 (&p)[2]) { asm volatile("s_nop 2" : "+v"(p[0]), "+v"(p[1])); }
-
-// O^T[32 columns of block d] += V^T P^T for one 16-key half of a tile.
-__device__ __forceinline__ void pv_mfma(f32x16& o, const bf16x8& v, const bf16x8& p) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(p));
-}
-
 // Masks the scores of keys past this lane's row position: score s[i] is tile key
 // 16 (i / 8) + 4 (i % 4) + 2 ((i / 4) % 2) + half, visible when <= rel_h + half (the row's
 // position minus the tile's first key; a negative value masks the whole tile).
@@ -132,46 +112,6 @@ __device__ __forceinline__ void causal_mask(f32x16& s, int rel_h) {
         s[i] = off <= rel_h ? s[i] : -INFINITY;
     }
 }
-
-// Softmax of one tile for this lane's row, split into pieces that interleave with the 32 P V
-// MFMAs of the previous tile: pieces 0-8 the row max, the reference (set by the first tile
-// with a visible key) and whether the max passed the reference's slack; 9-24 the
-// probabilities against the reference (rounded to bf16) and their sum.
-struct Softmax {
-    float a[8], mloc, mn, mu, x[16], l;
-    bool over;
-    __device__ __forceinline__ void piece(int k, const f32x16& s, float m_ref, float scale_log2, bf16x8 (&pk)[2]) {
-        if (k < 4) {
-            a[2 * k] = fmaxf(s[4 * k], s[4 * k + 1]);
-            a[2 * k + 1] = fmaxf(s[4 * k + 2], s[4 * k + 3]);
-        } else if (k == 4) {
-            a[0] = fmaxf(a[0], a[1]);
-            a[2] = fmaxf(a[2], a[3]);
-        } else if (k == 5) {
-            a[4] = fmaxf(a[4], a[5]);
-            a[6] = fmaxf(a[6], a[7]);
-        } else if (k == 6) {
-            a[0] = fmaxf(fmaxf(a[0], a[2]), fmaxf(a[4], a[6]));
-        } else if (k == 7) {
-            a[0] = fmaxf(a[0], half_swap(a[0]));
-        } else if (k == 8) {
-            mloc = a[0] * scale_log2;
-            mn = m_ref == -INFINITY ? mloc : m_ref;
-            over = mloc > mn + kRefSlack;
-            mu = mn == -INFINITY ? 0.0f : mn;
-            l = 0.0f;
-        } else if (k < 17) {
-            const int j = k - 9;  // scores 2j, 2j+1
-            x[2 * j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * j], scale_log2, -mu));
-            x[2 * j + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * j + 1], scale_log2, -mu));
-        } else if (k < 25) {
-            const int j = k - 17;
-            pk[j >> 2][2 * (j & 3)] = (__bf16)x[2 * j];
-            pk[j >> 2][2 * (j & 3) + 1] = (__bf16)x[2 * j + 1];
-            l += x[2 * j] + x[2 * j + 1];
-        }
-    }
-};
 
 template <bool PAGED>
 __global__ __launch_bounds__(NT, 1) void dense_wide_kernel(

@@ -19,15 +19,14 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_pcp.so")
 
 SOURCES = ["api.hip", "partition.hip", "kv_insert.hip", "merge.hip", "attn_dense.hip", "attn_dense_wide.hip",
-           "attn_sparse.hip", "attn_sparse_wide.hip", "topk_select.hip", "split_plan.hip"]
+           "attn_sparse_wide.hip", "topk_select.hip", "split_plan.hip"]
 
 # Per-file flags. The attention kernels' builtin MFMAs accumulate in VGPRs (MFMA VGPR form):
 # the scores everywhere, and O in the 64-row kernels, whose rare rescale is then plain VALU
-# work while Q sits in AGPRs; the wide kernels (512 + 64 dense, sparse over bf16 rows) keep O
+# work while Q sits in AGPRs; the wide kernels (512 + 64 dense, sparse) keep O
 # in AGPRs through inline-asm P V MFMAs instead.
 EXTRA = {"attn_dense.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_dense_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "attn_sparse.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "attn_sparse_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"

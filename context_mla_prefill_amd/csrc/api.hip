@@ -228,8 +228,7 @@ mla_status mla_prefill_partial(const mla_partial_args* a, void* stream) {
     if (!aligned16(a->q) || !aligned16(a->latent_kv) || !aligned16(a->rope_k) || !aligned16(a->o_partial))
         return fail(MLA_ERR_INVALID_ARG, "mla_prefill_partial: q/KV/output must be 16-byte aligned");
     hipError_t e = !sparse ? launch_dense_partial(*a, (hipStream_t)stream)
-                   : a->kv_dtype == MLA_KV_FP8_E4M3 ? launch_sparse_partial(*a, (hipStream_t)stream)
-                                                    : launch_sparse_wide_partial(*a, (hipStream_t)stream);
+                   : launch_sparse_wide_partial(*a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "mla_prefill_partial: %s", hipGetErrorString(e));
     return MLA_OK;
 }

@@ -1,10 +1,12 @@
-// Rank-local sparse MLA partial attention over bf16 latent rows -- a bf16 cache, or the
-// workspace that pcp_kv_dequant_fp8 fills from an fp8 cache once per step (sparse BF16 CP prefill
-// on a dequantised workspace: "DeepSeek-V4.1: Prefill support CP with multistream forward
-// prepare (4/N)", commit list, "Reuse shared compressed KV dequantization in V4.1 CP prefill";
-// the partial itself: "[DeepSeekV4][PCP] Enable context-parallel prefill for hybrid KV and
-// MegaMoE", "Purpose"). The key set of a query is that of sparse_keys.h: its selected indices in
-// [0, p] outside the window, plus the window, inside the key range of its split.
+// Rank-local sparse MLA partial attention ("[DeepSeekV4][PCP] Enable context-parallel prefill
+// for hybrid KV and MegaMoE", "Purpose") over bf16 latent rows -- a bf16 cache, or the workspace
+// that pcp_kv_dequant_fp8 fills from an fp8 cache once per step (sparse BF16 CP prefill on a
+// dequantised workspace: "DeepSeek-V4.1: Prefill support CP with multistream forward prepare
+// (4/N)", commit list, "Reuse shared compressed KV dequantization in V4.1 CP prefill") -- or
+// over an fp8-e4m3 cache with one fp32 scale per 64 rows, dequantised in the kernel (fp8 MLA
+// cache, block 64: "[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch Arguments").
+// The key set of a query is that of sparse_keys.h: its selected indices in [0, p] outside the
+// window, plus the window, inside the key range of its split.
 //
 // Work decomposition
 //  * A workgroup of two waves owns one token and a group of up to 64 heads (and one key range
@@ -22,6 +24,15 @@
 //    then (paged) the block-table entries of their keys, then the rows themselves.
 //  * Per tile: S^T = K Q^T (36 MFMAs), the key mask, the softmax against the fixed reference,
 //    O^T += V^T P^T (32 MFMAs); one barrier per tile.
+//  * fp8 cache (FP8): one bf16 tile buffer and two staging slots (74 + 5 KB of LDS with the
+//    rope rows and scales: still two workgroups per CU). A tile's fp8 rows (two keys per
+//    wave-wide load), rope rows and 64-row scales are gathered two tiles ahead into a slot; at
+//    the top of its step the workgroup dequantises the slot into the tile buffer,
+//    bf16_rne(fp32(e4m3) * scale), the arithmetic of pcp_kv_dequant_fp8, so the two paths give
+//    the same bf16 tiles and the same partials bit for bit. The dequantisation runs between
+//    barriers; the gathers have two tiles of compute to land.
+#include <type_traits>
+
 #include "sparse_keys.h"
 #include "wide_tile.h"
 
@@ -46,23 +57,56 @@ constexpr int QK_AHEAD = 4;           // Q K^T operand reads in flight
 constexpr int PV_AHEAD = 2;           // P V MFMAs' worth of V^T reads in flight
 constexpr int SEL_TILES = MAX_TOPK / TK;
 static_assert(SEL_TILES == 64, "one bit per selected-index tile in a 64-bit mask");
-static_assert(TILE_BYTES >= Q_REGION_BYTES && TILE_BYTES >= 32 * DL * 2,
+static_assert(TILE_BYTES >= 32 * Q_CHUNKS * 16 && TILE_BYTES >= 32 * DL * 2,
               "a wave's Q rows and O rows fit a tile buffer");
 static_assert(2 * TILE_BYTES + 1024 <= 160 * 1024 / 2, "two workgroups per CU");
 static_assert(2 * (LAT_PER_WAVE + ROPE_PER_WAVE) == KB, "one load after every second Q K^T MFMA");
+// fp8 staging slot: the 32 keys' E4M3 latent rows (512 bytes each), their bf16 rope rows (in the
+// tile buffer's swizzled order) and the 64-row scale of each key.
+constexpr int ST_ROPE = TK * DL;
+constexpr int ST_SCALE = ST_ROPE + TK * DR * 2;
+constexpr int STAGE_BYTES = ST_SCALE + TK * 4;
+constexpr int LAT8_PER_WAVE = TK / 4;                              // fp8 latent loads (two keys each)
+constexpr int FP8_LOADS = LAT8_PER_WAVE + ROPE_PER_WAVE + 1;       // per wave and tile, with the scales
+constexpr int Q_HALF = 16 * Q_CHUNKS * 16;                         // 16 Q rows
+constexpr int O_HALF = 16 * DL * 2;                                // 16 O rows
+static_assert(STAGE_BYTES >= Q_HALF && STAGE_BYTES >= O_HALF, "16 Q or O rows fit a staging slot");
+static_assert(TILE_BYTES + 2 * STAGE_BYTES + 2048 <= 160 * 1024 / 2, "two fp8 workgroups per CU");
+static_assert(FP8_LOADS <= KB / 3, "one fp8 load after every third Q K^T MFMA");
 
-template <bool PAGED>
+// bf16_rne(fp32(e4m3) * sc) of the 16 E4M3FN codes of w (OCP decode on gfx950), in order.
+__device__ __forceinline__ void dequant16(const uint4& w, float sc, bf16x8& lo, bf16x8& hi) {
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(wv[j], false);  // bytes 0, 1 of the word
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(wv[j], true);   // bytes 2, 3
+        bf16x8& o = j < 2 ? lo : hi;
+        const int e = 4 * (j & 1);
+        o[e] = (__bf16)(a[0] * sc);
+        o[e + 1] = (__bf16)(a[1] * sc);
+        o[e + 2] = (__bf16)(b[0] * sc);
+        o[e + 3] = (__bf16)(b[1] * sc);
+    }
+}
+
+template <bool PAGED, bool FP8>
 __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
-    const __bf16* __restrict__ q, const char* __restrict__ lat, const char* __restrict__ rope,
+    const __bf16* __restrict__ q, const char* __restrict__ lat, const float* __restrict__ kv_scale,
+    const char* __restrict__ rope,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vrow_kv_start, const int32_t* __restrict__ positions,
     const int32_t* __restrict__ topk_idx, int topk, int window, int n_vrows, int H, int64_t N_kv, float scale_log2,
     __bf16* __restrict__ o_out, float* __restrict__ lse_out, int kv_splits, int64_t split_stride,
     const int32_t* __restrict__ vrow_kv_len, const int32_t* __restrict__ block_table, int bt_stride,
     const int32_t* __restrict__ vrow_req, const int32_t* __restrict__ vrow_splits) {
-    // Tile buffers: two separate LDS objects, so the compiler can tell that loads streaming into
-    // one never touch the other. Each first holds one wave's Q rows, last its O rows.
+    // bf16 rows: two tile buffers. fp8 rows: the tile buffer kv0 and two staging slots. Separate
+    // LDS objects, so the compiler can tell that loads streaming into one never touch another.
+    // kv0 first holds wave 0's Q rows and last its O rows; wave 1's are in kv1 (bf16) or in the
+    // two staging slots, 16 rows each (fp8).
+    constexpr int KV1_BYTES = FP8 ? STAGE_BYTES : TILE_BYTES;
     __shared__ __attribute__((aligned(1024))) char kv0[TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char kv1[TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char kv1[KV1_BYTES];
+    __shared__ __attribute__((aligned(16))) char kv2[FP8 ? STAGE_BYTES : 16];
     __shared__ uint64_t s_live[2];
     __shared__ int s_redo[2];
 
@@ -86,19 +130,38 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     // packed, the cache's first row when paged); the caller keeps N_kv * DL * 2 below 2^32.
     // Every row is clamped into the cache before an offset is formed from it (a paged block id
     // outside the cache reads a wrong row of the cache, never memory outside it).
+    constexpr int LAT_ROW = FP8 ? DL : DL * 2;  // bytes of a cached latent row
     const int64_t row_base = PAGED ? 0 : wk.kv0;
     const int last_row = (int)(N_kv - 1 - row_base);
     const __amdgpu_buffer_rsrc_t lat_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(lat + row_base * (DL * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DL * 2)), kBufferFlags);
+        (void*)(lat + row_base * LAT_ROW), 0, (int)(uint32_t)((N_kv - row_base) * LAT_ROW), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)kv_scale, 0, FP8 ? (int)(uint32_t)(((N_kv + 63) / 64) * 4) : 0, kBufferFlags);
     const __amdgpu_buffer_rsrc_t rope_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(rope + row_base * (DR * 2)), 0, (int)(uint32_t)((N_kv - row_base) * (DR * 2)), kBufferFlags);
     const int32_t* bt_row = PAGED ? block_table + (int64_t)vrow_req[wk.lo_v] * bt_stride : nullptr;
 
-    // Q rows of this wave into its tile buffer; in flight while the live-tile mask is built.
-    char* const q_region = wave == 0 ? kv0 : kv1;
-    dma_q_rows<1>(__builtin_amdgcn_make_buffer_rsrc((void*)(q + (int64_t)wk.tok * H * DQK), 0, H * DQK * 2,
-                                                    kBufferFlags),
-                  wk.hg * BM + wave * 32, H, q_region, 0, lane);
+    // This wave's 32 Q rows (at the start) and O rows (at the end) in two halves of 16 rows:
+    // adjacent in its tile buffer, or for wave 1 over fp8 rows one half per staging slot.
+    char* const r_lo = wave == 0 ? kv0 : kv1;
+    char* const q_hi = FP8 && wave == 1 ? kv2 : r_lo + Q_HALF;
+    char* const o_hi = FP8 && wave == 1 ? kv2 : r_lo + O_HALF;
+    // Q rows: whole-row direct-to-LDS copies (16 rows are 18 loads), in flight while the
+    // live-tile mask is built; chunk c of row r at chunk r * 72 + (c ^ q_swizzle(r)) of its half.
+    {
+        const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + (int64_t)wk.tok * H * DQK), 0, H * DQK * 2, kBufferFlags);
+        const int row0 = wk.hg * BM + wave * 32;
+#pragma unroll
+        for (int i = 0; i < 2 * Q_HALF / 1024; ++i) {
+            const int L = 64 * i + lane;
+            const int r = L / Q_CHUNKS;
+            const int c = (L - r * Q_CHUNKS) ^ q_swizzle(r);
+            const int row = min(row0 + r, H - 1);  // rows past H read row H-1 (never stored)
+            lds_dma16(q_rsrc, (uint32_t)(row * (Q_CHUNKS * 16) + c * 16),
+                      i < Q_HALF / 1024 ? r_lo + 1024 * i : q_hi + 1024 * (i - Q_HALF / 1024));
+        }
+    }
 
     // The key set in this key range. A selected index counts when it lies in [key_lo, key_hi),
     // in [0, p] and before the window (the window supplies its own keys).
@@ -132,7 +195,13 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     const uint64_t live = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(live_v >> 32)) << 32) |
                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)live_v);
     bf16x8 qf[KB];
-    read_q_frags(q_region, lane, qf);
+    {
+        const int r = l32;
+        const char* qb = r < 16 ? r_lo + 16 * (r * Q_CHUNKS) : q_hi + 16 * ((r - 16) * Q_CHUNKS);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            qf[kb] = *reinterpret_cast<const bf16x8*>(qb + 16 * ((2 * kb + half) ^ q_swizzle(r)));
+    }
     lds_barrier();  // both waves hold their Q fragments: the tiles may overwrite the Q rows
 
     // Tiles: [0, n_sel) selected indices, then the window's; t_end ends the sequence. The live
@@ -219,7 +288,7 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     // swizzle the Q K^T rope reads expect. rope_src gives each lane's source offsets.
     auto lat_load = [&](char* dst, int rows, int i) __attribute__((always_inline)) {
         const int n = 2 * i + wave;
-        const uint32_t soff = (uint32_t)__builtin_amdgcn_readlane(rows, n) * (DL * 2);
+        const uint32_t soff = (uint32_t)__builtin_amdgcn_readlane(rows, n) * LAT_ROW;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(dst + n * LAT_STRIDE), 16, lane * 16, soff, 0,
                                                  0);
     };
@@ -231,9 +300,58 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
             ro[i] = (uint32_t)__shfl(rows, r) * (DR * 2) + c * 16;
         }
     };
-    auto rope_load = [&](char* dst, uint32_t voff, int i) __attribute__((always_inline)) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rsrc, (lds_void*)(dst + ROPE_OFF + (2 * wave + i) * 1024), 16,
+    auto rope_load = [&](char* rope_dst, uint32_t voff, int i) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rope_rsrc, (lds_void*)(rope_dst + (2 * wave + i) * 1024), 16,
                                                  voff, 0, 0, 0);
+    };
+    // fp8 rows into a staging slot: latent load i (0..7) of this wave fills slots n = 4 i + 2 wave
+    // (lanes 0-31) and n + 1 (lanes 32-63), 512 bytes each; the scale of slot 16 wave + l comes
+    // from lane l < 16 (scale_src gives each lane's source offset).
+    auto lat8_load = [&](char* st, int rows, int i) __attribute__((always_inline)) {
+        const int n = 4 * i + 2 * wave;
+        const int ra = __builtin_amdgcn_readlane(rows, n), rb = __builtin_amdgcn_readlane(rows, n + 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lat_rsrc, (lds_void*)(st + n * DL), 16,
+                                                 (uint32_t)(half ? rb : ra) * DL + l32 * 16, 0, 0, 0);
+    };
+    auto scale_src = [&](int rows) __attribute__((always_inline)) -> uint32_t {
+        return (uint32_t)((row_base + __shfl(rows, 16 * wave + (lane & 15))) >> 6) * 4;
+    };
+    auto scale_load = [&](char* st, uint32_t voff) __attribute__((always_inline)) {
+        if (lane < 16)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(scale_rsrc, (lds_void*)(st + ST_SCALE + 64 * wave), 4, voff, 0,
+                                                     0, 0);
+    };
+    // A staging slot into the tile buffer kv0: each thread converts 8 chunks of 16 codes (chunk
+    // k: tile row k / 32, codes 16 (k % 32) ..) in two batches of 4, a batch's reads all issued
+    // before any is converted; the rope rows are copied.
+    auto dequant = [&](const char* st) __attribute__((always_inline)) {
+        constexpr int NCH = TK * DL / 16 / NTW, BATCH = 4;
+        static_assert(NCH % BATCH == 0, "whole batches");
+#pragma unroll
+        for (int b0 = 0; b0 < NCH; b0 += BATCH) {
+            uint4 raw[BATCH];
+            float sc[BATCH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int k = (b0 + i) * NTW + tid;
+                raw[i] = *reinterpret_cast<const uint4*>(st + 16 * k);
+                sc[i] = *reinterpret_cast<const float*>(st + ST_SCALE + 4 * (k >> 5));
+            }
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int k = (b0 + i) * NTW + tid;
+                bf16x8 lo, hi;
+                dequant16(raw[i], sc[i], lo, hi);
+                char* const dst = kv0 + (k >> 5) * LAT_STRIDE + 32 * (k & 31);
+                *reinterpret_cast<bf16x8*>(dst) = lo;
+                *reinterpret_cast<bf16x8*>(dst + 16) = hi;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < TK * DR * 2 / 16 / NTW; ++j) {
+            const int k = j * NTW + tid;
+            *reinterpret_cast<uint4*>(kv0 + ROPE_OFF + 16 * k) = *reinterpret_cast<const uint4*>(st + ST_ROPE + 16 * k);
+        }
     };
 
     f32x16 acc_o[NBO];
@@ -242,10 +360,11 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     float l_run = 0.0f;        // running sum over this lane's share of the keys
     bool over = false;         // a score of this row passed the reference's slack
 
-    // Q K^T of the tile in kvt, with the next tile's loads (rows `rows`, into nxt) one after
-    // every second MFMA, so the vector memory pipe drains them under the matrix core.
-    auto qk_tile = [&](const char* kvt, const LaneOffs& lo, char* nxt, int rows, const uint32_t (&ro)[ROPE_PER_WAVE])
+    // Q K^T of the tile in kvt, with a later tile's NLOADS loads (issue_loads) one after every
+    // GAP-th MFMA, so the vector memory pipe drains them under the matrix core.
+    auto qk_tile = [&](const char* kvt, const LaneOffs& lo, auto issue_loads, auto nloads, auto gap)
         __attribute__((always_inline)) {
+        constexpr int NLOADS = decltype(nloads)::value, GAP = decltype(gap)::value;
         bf16x8 qa[KB];
         auto rd = [&](int kb) __attribute__((always_inline)) {
             const char* ap = kb < KBL ? kvt + lo.lat + kb * 32 : kvt + lo.rope[kb - KBL];
@@ -253,10 +372,7 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         };
         f32x16 s = f32x16{};
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < LAT_PER_WAVE; ++i) lat_load(nxt, rows, i);
-#pragma unroll
-        for (int i = 0; i < ROPE_PER_WAVE; ++i) rope_load(nxt, ro[i], i);
+        issue_loads();
 #pragma unroll
         for (int kb = 0; kb < QK_AHEAD; ++kb) rd(kb);
 #pragma unroll
@@ -269,7 +385,7 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         for (int k = 0; k < KB; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (k + QK_AHEAD < KB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (k % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (k % GAP == 0 && k / GAP < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         return s;
@@ -301,25 +417,13 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         }
     };
 
-    // Pipeline state entering a step: tile t0 (its rows in buffer cur, its valid-slot bits
-    // okb0), tile t1 past stage b (key1, okb1, paged block id blk1), tile t2 past stage a (ia2).
-    int t0, t1, t2, key1, blk1, ia2;
-    uint64_t okb0, okb1;
-    auto step = [&](const char* cur, char* nxt) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t0's rows and the pipeline's loads landed
-        __syncthreads();                     // ... for both waves; buffer nxt is free
-        const int rows1 = stage_c(key1, blk1);
-        uint32_t ro[ROPE_PER_WAVE];
-        rope_src(rows1, ro);
-        bool ok2;
-        const int key2 = stage_b(t2, ia2, ok2);
-        const uint64_t okb2 = __ballot(ok2);
-        const int blk2 = stage_b_load(key2);
-        const int t3 = next_tile(t2);
-        const int ia3 = stage_a(t3);
+    // One tile: scores, key mask (okb: its valid slots), softmax and P V on the tile in kvt, with
+    // a later tile's loads (issue_loads) among its Q K^T MFMAs.
+    auto compute_tile = [&](const char* kvt, uint64_t okb, auto issue_loads, auto nloads, auto gap)
+        __attribute__((always_inline)) {
         const LaneOffs lo = lane_offs();
-        f32x16 s = qk_tile(cur, lo, nxt, rows1, ro);
-        mask_keys(s, okb0, 0, half);
+        f32x16 s = qk_tile(kvt, lo, issue_loads, nloads, gap);
+        mask_keys(s, okb, 0, half);
         wide::Softmax sm;
         bf16x8 pn[2];
 #pragma unroll
@@ -328,15 +432,72 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         m_true = fmaxf(m_true, sm.mloc);
         over = over || sm.over;
         l_run += sm.l;
-        pv_tile(cur, lo, pn);
-        t0 = t1;
-        okb0 = okb1;
-        t1 = t2;
-        key1 = key2;
-        okb1 = okb2;
-        blk1 = blk2;
-        t2 = t3;
-        ia2 = ia3;
+        pv_tile(kvt, lo, pn);
+    };
+    // A tile's loads: bf16 rows into a tile buffer, or fp8 rows, rope rows and scales into a slot.
+    auto issue_bf16 = [&](char* dst, int rows, const uint32_t (&ro)[ROPE_PER_WAVE]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LAT_PER_WAVE; ++i) lat_load(dst, rows, i);
+#pragma unroll
+        for (int i = 0; i < ROPE_PER_WAVE; ++i) rope_load(dst + ROPE_OFF, ro[i], i);
+    };
+    auto issue_fp8 = [&](char* st, int rows, const uint32_t (&ro)[ROPE_PER_WAVE], uint32_t so)
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LAT8_PER_WAVE; ++i) lat8_load(st, rows, i);
+#pragma unroll
+        for (int i = 0; i < ROPE_PER_WAVE; ++i) rope_load(st + ST_ROPE, ro[i], i);
+        scale_load(st, so);
+    };
+
+    // Row pipeline across steps. D tiles separate the one computed and the one whose rows load
+    // during it (bf16: the next; fp8: the one after, two tiles ahead). Entering a step: tiles
+    // tq[0..D+1] of the sequence; okb[0..D] their valid-slot bits; tq[D] past stage b (key_d,
+    // blk_d); tq[D+1] past stage a (ia_n). A step runs stage c of tq[D] (its rows load during
+    // this step), stage b of tq[D+1] and stage a of the tile after it.
+    constexpr int D = FP8 ? 2 : 1;
+    int tq[D + 2], key_d, blk_d, ia_n;
+    uint64_t okb[D + 1];
+    auto step = [&](auto top, const char* kvt, char* dst) __attribute__((always_inline)) {
+        top();
+        const int rows = stage_c(key_d, blk_d);
+        uint32_t ro[ROPE_PER_WAVE];
+        rope_src(rows, ro);
+        const uint32_t so = FP8 ? scale_src(rows) : 0u;
+        bool ok;
+        const int key_n = stage_b(tq[D + 1], ia_n, ok);
+        const uint64_t okb_n = __ballot(ok);
+        const int blk_n = stage_b_load(key_n);
+        const int t_n = next_tile(tq[D + 1]);
+        const int ia_nn = stage_a(t_n);
+        if constexpr (FP8)
+            compute_tile(kvt, okb[0], [&]() __attribute__((always_inline)) { issue_fp8(dst, rows, ro, so); },
+                         std::integral_constant<int, FP8_LOADS>{}, std::integral_constant<int, 3>{});
+        else
+            compute_tile(kvt, okb[0], [&]() __attribute__((always_inline)) { issue_bf16(dst, rows, ro); },
+                         std::integral_constant<int, LAT_PER_WAVE + ROPE_PER_WAVE>{}, std::integral_constant<int, 2>{});
+#pragma unroll
+        for (int i = 0; i <= D; ++i) tq[i] = tq[i + 1];
+        tq[D + 1] = t_n;
+#pragma unroll
+        for (int i = 0; i < D; ++i) okb[i] = okb[i + 1];
+        okb[D] = okb_n;
+        key_d = key_n;
+        blk_d = blk_n;
+        ia_n = ia_nn;
+    };
+    // Step tops. bf16: tile tq[0]'s rows and the pipeline's loads landed for both waves, and the
+    // other buffer is free. fp8: all but the newest FP8_LOADS loads (the tile after the next, in
+    // the other slot) landed for both waves, so tq[0] is in its slot; the slot is dequantised
+    // into the tile buffer, which the barrier after it completes and the slot frees.
+    auto top_bf16 = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    };
+    auto top_fp8 = [&](const char* st) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(FP8_LOADS) : "memory");
+        dequant(st);
+        lds_barrier();
     };
 
     // Pass 0 against first-tile references; pass 1 only if some row of the workgroup passed its
@@ -346,35 +507,49 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         for (int d = 0; d < NBO; ++d) wide::o_zero(acc_o[d]);
         l_run = 0.0f;
         m_ref = pass == 0 ? -INFINITY : m_true;
-        t0 = next_tile(-1);
-        t1 = next_tile(t0);
-        t2 = next_tile(t1);
-        if (t0 < t_end) {  // workgroup-uniform; no key leaves O = 0, LSE = -inf
-            const int ia0 = stage_a(t0), ia1 = stage_a(t1);
-            ia2 = stage_a(t2);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            bool ok0, ok1;
-            const int key0 = stage_b(t0, ia0, ok0);
-            okb0 = __ballot(ok0);
-            const int blk0 = stage_b_load(key0);
-            key1 = stage_b(t1, ia1, ok1);
-            okb1 = __ballot(ok1);
-            blk1 = stage_b_load(key1);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            const int rows0 = stage_c(key0, blk0);
-            uint32_t ro[ROPE_PER_WAVE];
-            rope_src(rows0, ro);
+        tq[0] = next_tile(-1);
 #pragma unroll
-            for (int i = 0; i < LAT_PER_WAVE; ++i) lat_load(kv0, rows0, i);
+        for (int i = 1; i <= D + 1; ++i) tq[i] = next_tile(tq[i - 1]);
+        if (tq[0] < t_end) {  // workgroup-uniform; no key leaves O = 0, LSE = -inf
+            // fill the pipeline: stages a, b of tq[0..D+1], then the loads of tq[0..D-1]
+            int ia[D + 2], key[D + 1], blk[D + 1];
 #pragma unroll
-            for (int i = 0; i < ROPE_PER_WAVE; ++i) rope_load(kv0, ro[i], i);
-            // tile i of the sequence sits in buffer i % 2; past the last live tile the pipeline
-            // loads pad rows into the unused buffer
+            for (int i = 0; i <= D + 1; ++i) ia[i] = stage_a(tq[i]);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+#pragma unroll
+            for (int i = 0; i <= D; ++i) {
+                bool ok;
+                key[i] = stage_b(tq[i], ia[i], ok);
+                okb[i] = __ballot(ok);
+                blk[i] = stage_b_load(key[i]);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            key_d = key[D];
+            blk_d = blk[D];
+            ia_n = ia[D + 1];
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                const int rows = stage_c(key[i], blk[i]);
+                uint32_t ro[ROPE_PER_WAVE];
+                rope_src(rows, ro);
+                if constexpr (FP8)
+                    issue_fp8(i == 0 ? kv1 : kv2, rows, ro, scale_src(rows));
+                else
+                    issue_bf16(kv0, rows, ro);
+            }
+            // tile j of the sequence sits in buffer (bf16) or slot (fp8) j % 2; past the last
+            // live tile the pipeline loads pad rows
             while (true) {
-                step(kv0, kv1);
-                if (t0 >= t_end) break;
-                step(kv1, kv0);
-                if (t0 >= t_end) break;
+                if constexpr (FP8)
+                    step([&]() __attribute__((always_inline)) { top_fp8(kv1); }, kv0, kv1);
+                else
+                    step(top_bf16, kv0, kv1);
+                if (tq[0] >= t_end) break;
+                if constexpr (FP8)
+                    step([&]() __attribute__((always_inline)) { top_fp8(kv2); }, kv0, kv2);
+                else
+                    step(top_bf16, kv1, kv0);
+                if (tq[0] >= t_end) break;
             }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // loads issued after the last tile landed before LDS is reused
@@ -394,8 +569,10 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     // 2l + 1 ^ r, swapped when r is odd.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    char* const region = wave == 0 ? kv0 : kv1;
-    char* const lrow = region + l32 * (DL * 2);
+    auto o_row = [&](int r) __attribute__((always_inline)) {
+        return r < 16 ? r_lo + r * (DL * 2) : o_hi + (r - 16) * (DL * 2);
+    };
+    char* const lrow = o_row(l32);
 #pragma unroll
     for (int d = 0; d < NBO; ++d) {
 #pragma unroll
@@ -413,20 +590,21 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
         if (r >= n_valid) break;  // wave-uniform
-        uint4 v = *reinterpret_cast<const uint4*>(region + r * (DL * 2) + 16 * (lane ^ (r >> 1)));
+        uint4 v = *reinterpret_cast<const uint4*>(o_row(r) + 16 * (lane ^ (r >> 1)));
         if (r & 1) v = uint4{v.z, v.w, v.x, v.y};
         *reinterpret_cast<uint4*>(o_wave + r * DL) = v;
     }
     sched::mark_empty_slices(lse0, grow, valid && half == 0, wk.split, wk.nsplit, kv_splits, split_stride, H);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool FP8>
 hipError_t launch_wide(const mla_partial_args& a, hipStream_t stream) {
     const int64_t grid = (int64_t)a.T_loc * ((a.H + BM - 1) / BM) * a.kv_splits;
-    hipLaunchKernelGGL((sparse_wide_kernel<PAGED>), dim3((unsigned)grid), dim3(NTW), 0, stream, (const __bf16*)a.q,
-                       (const char*)a.latent_kv, (const char*)a.rope_k, a.cu_seqlens_q, a.vrow_kv_start, a.positions,
-                       a.topk_idx, a.topk, a.window, a.n_vrows, a.H, a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial,
-                       a.lse, a.kv_splits, a.split_stride, a.vrow_kv_len, a.block_table, a.bt_stride, a.vrow_req,
+    hipLaunchKernelGGL((sparse_wide_kernel<PAGED, FP8>), dim3((unsigned)grid), dim3(NTW), 0, stream,
+                       (const __bf16*)a.q, (const char*)a.latent_kv, a.kv_scale, (const char*)a.rope_k,
+                       a.cu_seqlens_q, a.vrow_kv_start, a.positions, a.topk_idx, a.topk, a.window, a.n_vrows, a.H,
+                       a.N_kv, a.scale * kLog2e, (__bf16*)a.o_partial, a.lse, a.kv_splits, a.split_stride,
+                       a.vrow_kv_len, a.block_table, a.bt_stride, a.vrow_req,
                        a.kv_splits > 1 ? a.vrow_splits : nullptr);
     return hipGetLastError();
 }
@@ -434,7 +612,9 @@ hipError_t launch_wide(const mla_partial_args& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_sparse_wide_partial(const mla_partial_args& a, hipStream_t stream) {
-    return a.block_table ? launch_wide<true>(a, stream) : launch_wide<false>(a, stream);
+    if (a.kv_dtype == MLA_KV_FP8_E4M3)
+        return a.block_table ? launch_wide<true, true>(a, stream) : launch_wide<false, true>(a, stream);
+    return a.block_table ? launch_wide<true, false>(a, stream) : launch_wide<false, false>(a, stream);
 }
 
 }  // namespace mla

@@ -43,7 +43,6 @@ hipError_t launch_topk_select(const float* scores, int64_t ld, const int32_t* po
 
 hipError_t launch_dense_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_dense_wide_partial(const mla_partial_args& a, hipStream_t stream);
-hipError_t launch_sparse_partial(const mla_partial_args& a, hipStream_t stream);
 hipError_t launch_sparse_wide_partial(const mla_partial_args& a, hipStream_t stream);
 
 }  // namespace mla

@@ -73,18 +73,6 @@ def compare(name, got_o, got_lse, ref_o, ref_lse, o_tol, lse_tol):
     return info
 
 
-def paths_agree(name, o_a, lse_a, o_b, lse_b, o_tol, lse_tol):
-    """Two HIP paths on the same inputs (O as float64 arrays, LSE): -inf LSE (a split slice with
-    no key) in the same places, every other row within the tolerances of the other path's."""
-    lse_a = np.asarray(lse_a, dtype=np.float64)
-    lse_b = np.asarray(lse_b, dtype=np.float64)
-    empty = np.isneginf(lse_a)
-    assert np.array_equal(empty, np.isneginf(lse_b)), f"{name}: empty slices differ"
-    used = ~empty.reshape(empty.shape[0], -1).any(axis=1)
-    o_a, o_b = np.asarray(o_a)[used], np.asarray(o_b)[used]
-    return compare(name, o_a, lse_a[used], o_b, lse_b[used], o_tol, lse_tol)
-
-
 def sample_tokens(w, plan, n_random=512, seed=None):
     """First and last token of every DualChunkSwap chunk (every virtual row of every rank;
     a decode row is a virtual row of one token), and n_random uniform tokens."""

@@ -467,18 +467,16 @@ def test_sparse_small_all_rows(gpu_lib):
     run.check_values(np.arange(w.T_glob))
 
 
-def check_paths_agree(a, b, merged=False):
-    """The bf16 workspace path and the in-kernel fp8 path on the same inputs agree within the fp8
-    tolerance (partials, or the merged outputs). The two kernels tile the key sums differently
-    (32 and 64 keys per tile) and keep different running maxima, so their roundings differ; each
-    is checked against the oracle on its own."""
+def check_paths_identical(a, b, merged=False):
+    """The bf16 workspace path and the in-kernel fp8 path on the same inputs give the same
+    partials (or, split, the same merged outputs) bit for bit: the fp8 kernel dequantises each
+    tile with the workspace's arithmetic and then runs the same tile compute."""
     if merged:
-        return hp.paths_agree("workspace vs in-kernel merged", on.bf16_to_f64(host_bits(a.bufs.o)),
-                              a.bufs.lse.cpu().numpy(), on.bf16_to_f64(host_bits(b.bufs.o)), b.bufs.lse.cpu().numpy(),
-                              SPARSE_O_TOL, LSE_TOL)
-    return hp.paths_agree("workspace vs in-kernel partial", on.bf16_to_f64(host_bits(a.bufs.o_cat)),
-                          a.bufs.lse_cat.cpu().numpy(), on.bf16_to_f64(host_bits(b.bufs.o_cat)),
-                          b.bufs.lse_cat.cpu().numpy(), SPARSE_O_TOL, LSE_TOL)
+        assert torch.equal(a.bufs.o.view(torch.int16), b.bufs.o.view(torch.int16))
+        assert torch.equal(a.bufs.lse.view(torch.int32), b.bufs.lse.view(torch.int32))
+    else:
+        assert torch.equal(a.bufs.o_cat.view(torch.int16), b.bufs.o_cat.view(torch.int16))
+        assert torch.equal(a.bufs.lse_cat.view(torch.int32), b.bufs.lse_cat.view(torch.int32))
 
 
 SPARSE_EDGE = {
@@ -511,7 +509,7 @@ def test_sparse_edge_cases(gpu_lib, seed):
     # the same batch on the bf16 workspace
     ws = SparseRun(w, topk_rows=rows, workspace=True)
     ws.check_values(np.arange(w.T_glob))
-    check_paths_agree(ws, run)
+    check_paths_identical(ws, run)
 
 
 def split_ranges(L, S):
@@ -774,13 +772,13 @@ def test_split_kv_sparse(gpu_lib):
 def test_split_kv_sparse_per_row(gpu_lib):
     """Per-row split KV on both sparse paths: row range counts 1..3 (clamped) with NaN-poisoned
     partials; used slices against the oracle on their keys, unused slices LSE = -inf, the
-    merge against unsharded sparse attention, on both paths, which agree with each other."""
+    merge against unsharded sparse attention, on both paths, which are bit-identical."""
     w = synth.custom(312, [900, 1, 400], [900, 2500, 1300], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,
                      kv_dtype="fp8", latent_std=1.0)
     sp = custom_split_plan(w, 3, 312)
     run = SparseRun(w, kv_splits=3, split_plan=sp)
     ws = SparseRun(w, kv_splits=3, split_plan=sp, workspace=True)
-    check_paths_agree(ws, run, merged=True)
+    check_paths_identical(ws, run, merged=True)
     toks = np.arange(w.T_glob)
     ref = hp.oracle_sparse(w, run.plan, run.q_bits, run.lat_codes, run.kv_scale, run.rope_bits, run.topk,
                            run.sink, toks)
@@ -833,13 +831,14 @@ SPARSE_WS = {
 @pytest.mark.parametrize("seed", sorted(SPARSE_WS))
 def test_sparse_workspace_path(gpu_lib, seed):
     """The sparse path on a bf16 workspace dequantised once (pcp_kv_dequant_fp8) matches the
-    oracle and agrees with the in-kernel dequantisation (partials, or with split KV the merge)."""
+    oracle and gives the in-kernel dequantisation's partials (with split KV its merge) bit for
+    bit."""
     q, kv, P, H, topk, window, S = SPARSE_WS[seed]
     w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64, topk=topk, window=window, kv_dtype="fp8",
                      latent_std=1.0)
     fp8 = SparseRun(w, kv_splits=S)
     ws = SparseRun(w, kv_splits=S, workspace=True)
-    check_paths_agree(ws, fp8, merged=S > 1)
+    check_paths_identical(ws, fp8, merged=S > 1)
     if S == 1:
         ws.check_values(np.arange(w.T_glob))
     else:
@@ -853,12 +852,12 @@ def test_sparse_largest_window_and_topk(gpu_lib):
     """The largest key sets the API takes, top-k 2048 and a 4096-key window, on a prefill where
     early queries see the window cover their whole prefix (every selected index falls inside it
     and counts once) and late ones see 2048 selected keys before a full window: the fp8 kernel
-    and the bf16 workspace path each on sampled tokens against the oracle, in agreement, all finite."""
+    and the bf16 workspace path bit-identical, each on sampled tokens against the oracle, all finite."""
     w = synth.custom(221, [7000], [7000], P=2, H=64, Dl=512, Dr=64, topk=2048, window=4096, kv_dtype="fp8",
                      latent_std=1.0)
     fp8 = SparseRun(w)
     ws = SparseRun(w, workspace=True)
-    check_paths_agree(ws, fp8)
+    check_paths_identical(ws, fp8)
     toks = hp.sample_tokens(w, fp8.plan, n_random=48)
     print(f"[check] largest key sets: {len(toks)} sampled tokens", flush=True)
     for r in (fp8, ws):
@@ -903,13 +902,13 @@ def test_sparse_head_counts_under_64(gpu_lib, seed):
     """The sparse path at head counts that are not a multiple of 64 (per-GPU shares under
     tensor parallelism): the last head group's rows past H stay idle. Every row of every rank
     and the merge against the oracle, on both the in-kernel fp8 path and the bf16 workspace,
-    which agree with each other."""
+    which agree bit for bit."""
     q, kv, P, H, topk, window = SPARSE_HEADS[seed]
     w = synth.custom(seed, q, kv, P=P, H=H, Dl=512, Dr=64, topk=topk, window=window, kv_dtype="fp8",
                      latent_std=1.0)
     fp8 = SparseRun(w)
     ws = SparseRun(w, workspace=True)
-    check_paths_agree(ws, fp8)
+    check_paths_identical(ws, fp8)
     fp8.check_values(np.arange(w.T_glob))
     ws.check_values(np.arange(w.T_glob))
 

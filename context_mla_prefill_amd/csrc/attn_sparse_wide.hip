@@ -24,8 +24,8 @@
 //    then (paged) the block-table entries of their keys, then the rows themselves.
 //  * Per tile: S^T = K Q^T (36 MFMAs), the key mask, the softmax against the fixed reference,
 //    O^T += V^T P^T (32 MFMAs); one barrier per tile.
-//  * fp8 cache (FP8): one bf16 tile buffer and two staging slots (74 + 5 KB of LDS with the
-//    rope rows and scales: still two workgroups per CU). A tile's fp8 rows (two keys per
+//  * fp8 cache (FP8): one bf16 tile buffer (37 KB) and two 20 KB staging slots (78.6 KB of LDS:
+//    still two workgroups per CU). A tile's fp8 rows (two keys per
 //    wave-wide load), rope rows and 64-row scales are gathered two tiles ahead into a slot; at
 //    the top of its step the workgroup dequantises the slot into the tile buffer,
 //    bf16_rne(fp32(e4m3) * scale), the arithmetic of pcp_kv_dequant_fp8, so the two paths give
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     const bool valid = head < H;  // rows past H (a last head group under 64) stay idle
     const int64_t grow = (int64_t)wk.tok * H + head;
     // Buffer views of the latent and rope rows from row_base (the request's first row when
-    // packed, the cache's first row when paged); the caller keeps N_kv * DL * 2 below 2^32.
+    // packed, the cache's first row when paged) and of the 64-row scales; the caller keeps the
+    // cache's latent bytes below 2^32.
     // Every row is clamped into the cache before an offset is formed from it (a paged block id
     // outside the cache reads a wrong row of the cache, never memory outside it).
     constexpr int LAT_ROW = FP8 ? DL : DL * 2;  // bytes of a cached latent row

@@ -90,6 +90,28 @@ __device__ __forceinline__ void dequant16(const uint4& w, float sc, bf16x8& lo, 
     }
 }
 
+// The same values when sc is a power of two 2^e with -117 <= e <= 119: fp32(e4m3) * 2^e is
+// then exact in bf16 (4 significant bits; the nonzero E4M3FN magnitudes 2^-9 .. 448 times
+// such a scale stay normal and finite), and gfx950's scaled conversion computes it
+// directly, two codes per instruction (it applies the power of two of its scale operand).
+__device__ __forceinline__ void dequant16_pow2(const uint4& w, float sc, bf16x8& lo, bf16x8& hi) {
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[j], sc, false));
+        o[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[j], sc, true));
+    }
+    lo = __builtin_bit_cast(bf16x8, uint4{o[0], o[1], o[2], o[3]});
+    hi = __builtin_bit_cast(bf16x8, uint4{o[4], o[5], o[6], o[7]});
+}
+
+// sc is +2^e with -117 <= e <= 119 (the library's quantiser makes power-of-two scales).
+__device__ __forceinline__ bool pow2_scale(float sc) {
+    const uint32_t b = __float_as_uint(sc);
+    return ((b & 0x807FFFFFu) | (b - (10u << 23) > (236u << 23) ? 1u : 0u)) == 0;
+}
+
 template <bool PAGED, bool FP8>
 __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     const __bf16* __restrict__ q, const char* __restrict__ lat, const float* __restrict__ kv_scale,
@@ -328,26 +350,41 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     auto dequant = [&](const char* st) __attribute__((always_inline)) {
         constexpr int NCH = TK * DL / 16 / NTW, BATCH = 4;
         static_assert(NCH % BATCH == 0, "whole batches");
+        // the scales of this thread's chunks (chunk c: tile row (c NTW + tid) / 32); when all of
+        // the wave's are powers of two the scaled conversion does the tile (the library's
+        // quantiser writes such scales), else the multiply, with the same results
+        float sc[NCH];
+        uint32_t odd = 0;
 #pragma unroll
-        for (int b0 = 0; b0 < NCH; b0 += BATCH) {
-            uint4 raw[BATCH];
-            float sc[BATCH];
-#pragma unroll
-            for (int i = 0; i < BATCH; ++i) {
-                const int k = (b0 + i) * NTW + tid;
-                raw[i] = *reinterpret_cast<const uint4*>(st + 16 * k);
-                sc[i] = *reinterpret_cast<const float*>(st + ST_SCALE + 4 * (k >> 5));
-            }
-#pragma unroll
-            for (int i = 0; i < BATCH; ++i) {
-                const int k = (b0 + i) * NTW + tid;
-                bf16x8 lo, hi;
-                dequant16(raw[i], sc[i], lo, hi);
-                char* const dst = kv0 + (k >> 5) * LAT_STRIDE + 32 * (k & 31);
-                *reinterpret_cast<bf16x8*>(dst) = lo;
-                *reinterpret_cast<bf16x8*>(dst + 16) = hi;
-            }
+        for (int c = 0; c < NCH; ++c) {
+            sc[c] = *reinterpret_cast<const float*>(st + ST_SCALE + 4 * ((c * NTW + tid) >> 5));
+            odd |= pow2_scale(sc[c]) ? 0u : 1u;
         }
+        const bool fast = __builtin_amdgcn_ballot_w64(odd != 0) == 0;  // wave-uniform
+        auto convert = [&](auto fast_tag) __attribute__((always_inline)) {
+#pragma unroll
+            for (int b0 = 0; b0 < NCH; b0 += BATCH) {
+                uint4 raw[BATCH];
+#pragma unroll
+                for (int i = 0; i < BATCH; ++i) raw[i] = *reinterpret_cast<const uint4*>(st + 16 * ((b0 + i) * NTW + tid));
+#pragma unroll
+                for (int i = 0; i < BATCH; ++i) {
+                    const int k = (b0 + i) * NTW + tid;
+                    bf16x8 lo, hi;
+                    if constexpr (decltype(fast_tag)::value)
+                        dequant16_pow2(raw[i], sc[b0 + i], lo, hi);
+                    else
+                        dequant16(raw[i], sc[b0 + i], lo, hi);
+                    char* const dst = kv0 + (k >> 5) * LAT_STRIDE + 32 * (k & 31);
+                    *reinterpret_cast<bf16x8*>(dst) = lo;
+                    *reinterpret_cast<bf16x8*>(dst + 16) = hi;
+                }
+            }
+        };
+        if (fast)
+            convert(std::true_type{});
+        else
+            convert(std::false_type{});
 #pragma unroll
         for (int j = 0; j < TK * DR * 2 / 16 / NTW; ++j) {
             const int k = j * NTW + tid;

@@ -44,10 +44,22 @@ __global__ __launch_bounds__(256) void kv_insert_kernel(
 //      clear);
 //   2. one wave per row folds the row's max |x| into its block word with an atomic max
 //      when that word is pending (non-negative fp32 bits order like their values);
-//   3. one wave per row turns a pending word into the scale amax / 448 (1 when amax is 0)
-//      -- every row of a block computes the same value, so racing writers agree -- then
-//      writes its codes e4m3fn_rne(clamp(x / scale, -448, 448)) and copies its rope row.
+//   3. one wave per row turns a pending word into the scale, the smallest power of two not
+//      below fp32(amax / 448) and not below 2^-126 (1 when amax is 0) -- every row of a
+//      block computes the same value, so racing writers agree -- then writes its codes
+//      e4m3fn_rne(clamp(x / scale, -448, 448)) and copies its rope row.
+// A power-of-two scale costs at most one binade of the code range and makes each decoded
+// value code * scale exact in bf16, which the attention kernel converts two codes per
+// instruction.
 constexpr uint32_t kPending = 0x80000000u;
+
+// Smallest normal power of two >= r, for r >= 0 finite (2^-126 for r below it).
+__device__ __forceinline__ float pow2_at_least(float r) {
+    uint32_t b = __float_as_uint(r);
+    if (b < 0x00800000u) return __uint_as_float(0x00800000u);
+    if (b & 0x007FFFFFu) b = (b & 0x7F800000u) + 0x00800000u;
+    return __uint_as_float(b);
+}
 
 __global__ __launch_bounds__(256) void fp8_block_reset(const int32_t* __restrict__ slot, int T, int64_t N_kv,
                                                        uint32_t* __restrict__ scale_word) {
@@ -90,7 +102,7 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows(const __bf16* __restric
     float sc;
     if (w & kPending) {
         const float a = __uint_as_float(w & ~kPending);
-        sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+        sc = a > 0.0f ? pow2_at_least(__fdiv_rn(a, 448.0f)) : 1.0f;
         if (lane == 0) scale_word[s >> 6] = __float_as_uint(sc);
     } else {
         sc = __uint_as_float(w);

@@ -17,7 +17,8 @@ Workloads (the five shapes the path is measured and checked on):
 3. dense 128K: 1 request of 131072 tokens, 4 ranks, 16 heads, latent 512 + rope 64.
 4. sparse 128K: 1 request of 131072 tokens, 2 ranks, 64 heads, top-2048 keys drawn
    uniformly without replacement from the causal prefix plus a 128-token window,
-   latent KV stored as fp8-e4m3 with one fp32 scale per 64 packed KV rows.
+   latent KV stored as fp8-e4m3 with one power-of-two fp32 scale per 64 packed KV rows
+   (the library's quantise-on-insert rule).
 5. mixed varlen: 8 prefills with lengths log-uniform in [4096, 65536) and 64 decode
    rows (1 token each) with contexts log-uniform in [1024, 32768), 4 ranks, 16 heads.
 6. chunked prefill: one step of 32768 batched tokens, 4 ranks, 16 heads: the last 16384-
@@ -249,7 +250,8 @@ def kv_scales(w: Workload) -> np.ndarray:
 
 
 def _fp8_tiles(w: Workload, tile0: int, tile1: int, want_codes: bool = True):
-    """Quantise latent tiles [tile0, tile1) to E4M3FN: scale = amax(tile)/448, RNE + saturate.
+    """Quantise latent tiles [tile0, tile1) to E4M3FN: scale = the smallest power of two
+    (at least 2^-126) not below fp32(amax(tile)/448), 1 for an all-zero tile; RNE + saturate.
 
     The encoding is done by torch's float8_e4m3fn cast (a library routine): it only
     prepares the stored cache bytes, the way a cache writer would.
@@ -264,8 +266,11 @@ def _fp8_tiles(w: Workload, tile0: int, tile1: int, want_codes: bool = True):
     xp = np.concatenate([x, np.zeros((pad, w.Dl), np.float32)]) if pad else x
     tiles = xp.reshape(nt, FP8_TILE * w.Dl)
     amax = np.abs(tiles).max(axis=1)
-    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
-    scale[scale == 0] = np.float32(1.0)
+    r = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    m, e = np.frexp(r)  # r = m 2^e, 0.5 <= m < 1 (exact)
+    scale = np.ldexp(np.float32(1.0), np.where(m == 0.5, e - 1, e)).astype(np.float32)
+    scale = np.maximum(scale, np.float32(2.0**-126))
+    scale[amax == 0] = np.float32(1.0)
     if not want_codes:
         return None, scale
     t = torch.from_numpy(tiles) / torch.from_numpy(scale)[:, None]

@@ -141,7 +141,9 @@ mla_status pcp_kv_insert(const void* local_latent, const void* local_rope, const
  * Arguments": fp8 MLA KV cache, block size 64; the scale layout is this library's).
  * A block B is opened by the call that writes its first row (slot % 64 == 0); for it
  *   a = max |x| over the latent elements this call writes into B (as fp32),
- *   kv_scale[B] = a / 448 (fp32 division; 1 when a == 0).
+ *   kv_scale[B] = the smallest power of two 2^e >= fp32(a / 448) with e >= -126
+ *                 (1 when a == 0): a shared power-of-two scale, which makes every decoded
+ *                 value code * scale exact in bf16.
  * A block opened by an earlier call keeps its scale (a chunked prefill that continues a
  * block quantises against the scale its first chunk set). Every written element gets
  *   code = e4m3fn_rne(clamp(x / kv_scale[B], -448, 448)) (fp32 division, round to
@@ -220,7 +222,9 @@ mla_status sparse_topk_select(const float* scores, int64_t ld, const int32_t* po
  *   S_j = scale * <q[i][h], key_j>; O = softmax(S) @ latent (bf16, round to nearest
  *   even); LSE = log(sum_j exp(S_j)) (fp32, natural log). No sink.
  * fp8 latent: element = bf16_rne(fp32(e4m3(code)) * kv_scale[row / 64]) (row = KV row, so
- *   with paging one scale per block), dequantised inside the sparse kernel. A sparse call with
+ *   with paging one scale per block), dequantised inside the sparse kernel. Any positive
+ *   finite scales are taken; power-of-two scales 2^-117 .. 2^119 (those pcp_kv_insert_fp8
+ *   writes) dequantise faster, with the same results. A sparse call with
  *   bf16 latent (for instance the workspace of pcp_kv_dequant_fp8) gathers bf16 rows instead.
  * Split KV (kv_splits = S > 1): the key set of virtual row v is cut by key position into
  *   s_v ranges (s_v = vrow_splits[v], or S for every row when vrow_splits is NULL) and

@@ -8,9 +8,10 @@
 * fp8 MLA cache ("[Feature][PCP] Add DeepSeek-V4.1-Flash support", "vLLM Launch
   Arguments": fp8 MLA KV cache): OCP E4M3FN latent codes with one fp32 scale per 64-row
   block, rope kept bf16. The pages name the cache but not its layout; the reading taken
-  here is a block scale a / 448 with a the block's largest |x|, set by the insert that
-  writes the block's first row, later rows of the block quantised against that stored
-  scale with saturation at +-448.
+  here is a power-of-two block scale, the smallest one not below a / 448 with a the
+  block's largest |x| (shared power-of-two scales as in the OCP microscaling formats),
+  set by the insert that writes the block's first row, later rows of the block quantised
+  against that stored scale with saturation at +-448.
 """
 import numpy as np
 
@@ -26,6 +27,15 @@ def paged_rows(block_table: np.ndarray, b: int, positions: np.ndarray) -> np.nda
     return np.asarray(block_table, dtype=np.int64)[b, pos // BLOCK] * BLOCK + pos % BLOCK
 
 
+def pow2_at_least(r) -> np.float32:
+    """The smallest power of two 2^e >= r with e >= -126 (normal binary32), for r >= 0."""
+    r = float(np.float32(r))
+    e = -126
+    while 2.0 ** e < r:
+        e += 1
+    return np.float32(2.0 ** e)
+
+
 def quantize_insert_fp8(codes: np.ndarray, scales: np.ndarray, lat_bits: np.ndarray, slot: np.ndarray):
     """One quantise-on-insert call. Returns new (codes, scales); the inputs are not changed.
 
@@ -36,8 +46,9 @@ def quantize_insert_fp8(codes: np.ndarray, scales: np.ndarray, lat_bits: np.ndar
 
     Steps: (1) the blocks this call opens are those of slots s with s % 64 == 0;
     (2) for each, a = max |x| over the elements the call writes into it, and its scale
-    becomes fp32(a / 448), or 1 when a == 0; (3) each written element becomes
-    e4m3fn_rne(clamp(fp32(x / scale), -448, 448)) with its block's scale (new or stored).
+    becomes pow2_at_least(fp32(a / 448)), or 1 when a == 0; (3) each written element
+    becomes e4m3fn_rne(clamp(fp32(x / scale), -448, 448)) with its block's scale (new or
+    stored).
     """
     codes = np.array(codes, dtype=np.uint8, copy=True)
     scales = np.array(scales, dtype=np.float32, copy=True)
@@ -51,7 +62,7 @@ def quantize_insert_fp8(codes: np.ndarray, scales: np.ndarray, lat_bits: np.ndar
     opened = np.unique(blk[s % BLOCK == 0])
     for B in opened:
         a = np.float32(np.max(np.abs(x[blk == B]))) if np.any(blk == B) else np.float32(0.0)
-        scales[B] = np.float32(a) / np.float32(E4M3_MAX) if a > 0 else np.float32(1.0)
+        scales[B] = pow2_at_least(np.float32(a) / np.float32(E4M3_MAX)) if a > 0 else np.float32(1.0)
     sc = scales[blk][:, None]
     y = np.clip((x / sc).astype(np.float32), -E4M3_MAX, E4M3_MAX)
     codes[s] = on.e4m3fn_encode_rne(y)

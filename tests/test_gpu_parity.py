@@ -440,21 +440,48 @@ class SparseRun:
                    np.stack([ref[g][3] for g in toks]), o_tol, LSE_TOL)
 
 
-def test_fp8_dequant_bit_exact(gpu_lib):
+@pytest.mark.parametrize("scale", [0.3713, 2.0 ** -5, 2.0 ** -117, 2.0 ** -118, 2.0 ** 6])
+def test_fp8_dequant_bit_exact(gpu_lib, scale):
     """A query whose key set is one key returns that key's dequantised latent row exactly:
-    every finite E4M3FN code, times a non-power-of-two scale, rounded to bf16."""
+    every finite E4M3FN code times the block scale, rounded to bf16. Powers of two from 2^-117
+    up take the kernel's scaled conversion (products exact and normal), the others (2^-118:
+    subnormal products; 0.3713) its multiply."""
     w = synth.custom(201, [1], [1], P=1, H=64, Dl=512, Dr=64, topk=64, window=128, kv_dtype="fp8",
                      latent_std=1.0)
     codes = np.arange(512, dtype=np.int64) % 256
     codes[(codes & 0x7F) == 0x7F] = 0  # the two NaN codes
     lat = codes.astype(np.uint8)[None, :]
-    scale = np.array([0.3713], np.float32)
+    scale = np.array([scale], np.float32)
     run = SparseRun(w, lat_codes=lat, kv_scale=scale, topk_rows=np.full((1, 64), -1, np.int32))
     got = on.bf16_to_f64(host_bits(run.bufs.o_cat)[0])  # [H, 512]
     want = on.dequant_fp8_rows(lat, np.array([0]), scale)[0]
     bad = np.nonzero(got != want[None, :])
     assert len(bad[0]) == 0, f"codes {codes[bad[1][:8]]}: got {got[bad][:8]} want {want[bad[1][:8]]}"
     # exact equality of values (the sign of a zero is not carried through P V: +0 + -0 = +0)
+
+
+SCALE_KINDS = ("pow2_varied", "arbitrary", "mixed")
+
+
+@pytest.mark.parametrize("kind", SCALE_KINDS)
+def test_sparse_fp8_scale_kinds(gpu_lib, kind):
+    """Block scales beyond the quantiser's: powers of two that vary by block (2^-3 .. 2^0
+    times the drawn ones), arbitrary positive fp32 scales (0.3 .. 1 times them), and
+    alternating blocks of both (tiles then mix rows of either kind); no larger than the drawn
+    ones, so the values stay in the range the absolute bounds are set for. The in-kernel fp8
+    path against the oracle on every row, and bit-identical to the bf16 workspace path."""
+    w = synth.custom(231, [1200, 500], [1200, 800], P=2, H=64, Dl=512, Dr=64, topk=256, window=64,
+                     kv_dtype="fp8", latent_std=1.0)
+    rng = np.random.default_rng(231)
+    base = synth.kv_scales(w)
+    p2 = (base * np.exp2(rng.integers(-3, 1, base.shape))).astype(np.float32)
+    arb = (base * rng.uniform(0.3, 1.0, base.shape)).astype(np.float32)
+    scale = {"pow2_varied": p2, "arbitrary": arb,
+             "mixed": np.where(np.arange(base.size) % 2 == 0, p2, arb).astype(np.float32)}[kind]
+    run = SparseRun(w, kv_scale=scale)
+    run.check_values(np.arange(w.T_glob))
+    ws = SparseRun(w, kv_scale=scale, workspace=True)
+    check_paths_identical(ws, run)
 
 
 def test_sparse_small_all_rows(gpu_lib):

@@ -98,34 +98,36 @@ def test_quantize_scale_per_block_and_zero_block():
     # block 2 all zero
     cache, sc = _fresh(192, D)
     c2, s2 = ok.quantize_insert_fp8(cache, sc, synth.bf16_bits(x), np.arange(192))
-    assert s2[0] == np.float32(7.0) / np.float32(448) and s2[1] == np.float32(0.5) / np.float32(448)
+    # 7/448 = 2^-6 is a power of two; 0.5/448 lies in (2^-10, 2^-9]
+    assert s2[0] == np.float32(2.0 ** -6) and s2[1] == np.float32(2.0 ** -9)
     assert s2[2] == 1.0 and np.all(c2[128:] == 0)
     assert c2[10, 2] == 0xFE  # -448 after dividing by the block's own scale
-    assert np.all(c2[64:128] == 0x7E)  # every element is the block maximum
+    assert np.all(c2[64:128] == 0x78)  # every element is the block maximum, 0.5 / 2^-9 = 256
 
 
 def test_quantize_later_rows_use_the_stored_scale():
     """A block opened by a first call (rows 0..9) keeps its scale when a second call writes
-    rows 10..63; a value beyond 448 * scale saturates."""
+    rows 10..63; a value beyond 448 * scale saturates. (2/448 lies in (2^-8, 2^-7].)"""
     D = 8
     cache, sc = _fresh(64, D)
     a = np.full((10, D), 2.0, np.float32)
     c1, s1 = ok.quantize_insert_fp8(cache, sc, synth.bf16_bits(a), np.arange(10))
-    assert s1[0] == np.float32(2.0) / np.float32(448)
+    assert s1[0] == np.float32(2.0 ** -7)
     b = np.full((54, D), 1.0, np.float32)
-    b[3, 1] = 5.0  # 5 / (2/448) = 1120 -> saturates
+    b[3, 1] = 5.0  # 5 / 2^-7 = 640 -> saturates
     b[4, 2] = -5.0
     c2, s2 = ok.quantize_insert_fp8(c1, s1, synth.bf16_bits(b), np.arange(10, 64))
     assert s2[0] == s1[0] and np.array_equal(c2[:10], c1[:10])
     assert c2[13, 1] == 0x7E and c2[14, 2] == 0xFE
-    assert on.e4m3fn_decode(c2[10:11, 0])[0] == 224.0  # 1 / (2/448)
+    assert on.e4m3fn_decode(c2[10:11, 0])[0] == 128.0  # 1 / 2^-7
 
 
 def test_quantize_skips_rows_outside_the_cache():
     cache, sc = _fresh(64, 8)
     x = np.ones((3, 8), np.float32)
     c2, s2 = ok.quantize_insert_fp8(cache, sc, synth.bf16_bits(x), np.array([-1, 64, 0]))
-    assert np.all(c2[0] == 0x7E) and np.all(c2[1:] == 0x7F) and s2[0] == np.float32(1) / np.float32(448)
+    # 1/448 lies in (2^-9, 2^-8]: scale 2^-8, code of 256
+    assert np.all(c2[0] == 0x78) and np.all(c2[1:] == 0x7F) and s2[0] == np.float32(2.0 ** -8)
 
 
 def test_quantize_error_bound():
@@ -140,9 +142,27 @@ def test_quantize_error_bound():
     s = s2[np.arange(256) // 64].astype(np.float64)[:, None]
     err = np.abs(on.e4m3fn_decode(c2) * s - xe)
     assert np.all(err <= 2.0 ** -4 * np.abs(xe) + 2.0 ** -10 * s * (1 + 1e-6))
-    # the block scale is the block's max |x| / 448
+    # the block scale is a power of two with max|x| / 448 <= scale < 2 max|x| / 448 (the
+    # smallest such power; the block's largest element lands in (224, 448])
     for B in range(4):
-        assert s2[B] == np.float32(np.abs(xe[64 * B:64 * B + 64]).max()) / np.float32(448)
+        a = np.abs(xe[64 * B:64 * B + 64]).max() / 448.0
+        m, _ = np.frexp(np.float64(s2[B]))
+        assert m == 0.5 and a * (1 - 2.0 ** -23) <= s2[B] < 2 * a
+
+
+def test_pow2_at_least():
+    """Powers of two map to themselves, anything above one to the next, and everything at or
+    below 2^-126 (zero and subnormals included) to 2^-126."""
+    for e in (-126, -40, -6, 0, 1, 100):
+        p = np.float32(2.0 ** e)
+        assert ok.pow2_at_least(p) == p
+        up = np.nextafter(p, np.float32(np.inf))
+        assert ok.pow2_at_least(up) == np.float32(2.0 ** (e + 1))
+        if e > -126:
+            assert ok.pow2_at_least(np.nextafter(p, np.float32(0))) == p
+    for r in (0.0, 1e-45, 2.0 ** -130):
+        assert ok.pow2_at_least(r) == np.float32(2.0 ** -126)
+    assert ok.pow2_at_least(0.3) == 0.5 and ok.pow2_at_least(200.0) == 256.0
 
 
 def test_paged_rows():

@@ -489,7 +489,8 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
     };
 
     // Row pipeline across steps. D tiles separate the one computed and the one whose rows load
-    // during it (bf16: the next; fp8: the one after, two tiles ahead). Entering a step: tiles
+    // during it (bf16: the next; fp8: the one after, two tiles ahead, so that a tile's rows
+    // load into one slot while the other slot still holds the next tile). Entering a step: tiles
     // tq[0..D+1] of the sequence; okb[0..D] their valid-slot bits; tq[D] past stage b (key_d,
     // blk_d); tq[D+1] past stage a (ia_n). A step runs stage c of tq[D] (its rows load during
     // this step), stage b of tq[D+1] and stage a of the tile after it.
@@ -525,15 +526,18 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         ia_n = ia_nn;
     };
     // Step tops. bf16: tile tq[0]'s rows and the pipeline's loads landed for both waves, and the
-    // other buffer is free. fp8: all but the newest FP8_LOADS loads (the tile after the next, in
-    // the other slot) landed for both waves, so tq[0] is in its slot; the slot is dequantised
-    // into the tile buffer, which the barrier after it completes and the slot frees.
+    // other buffer is free. fp8: every load issued so far landed for both waves, tq[0]'s (two
+    // steps old) and the next tile's (one step old, in the other slot); tq[0]'s slot is
+    // dequantised into the tile buffer, which the barrier after it completes and the slot
+    // frees. Waiting only for all but the newest FP8_LOADS loads would cover tq[0] if loads
+    // retired in issue order, but with such a wait alone reads of the slot saw rows that had
+    // not landed; the full wait measured no slower, the newest loads having had a step.
     auto top_bf16 = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     };
     auto top_fp8 = [&](const char* st) __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(FP8_LOADS) : "memory");
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         dequant(st);
         lds_barrier();
     };

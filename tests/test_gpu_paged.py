@@ -203,6 +203,45 @@ def test_dense_full_size_paged_sampled(gpu_lib, cfg):
                np.stack([ref[g][3] for g in toks]), O_TOL, LSE_TOL)
     assert bool(torch.isfinite(paged.bufs.o.float()).all()) and bool(torch.isfinite(paged.bufs.lse).all())
 
+def test_fp8_insert_scale_edges(gpu_lib):
+    """The power-of-two block scale at its edges, codes and scales bit for bit against the
+    oracle: amax / 448 exactly a power of two (2^-3, and 2^-117), one bf16 ulp above one
+    (the next power), below 2^-126 (the floor 2^-126), an all-zero block (1) and amax 2^100
+    (2^92). The other elements of a block are 0 or normal bf16 values below its maximum."""
+    Dl, Dr, N = 64, 16, 64 * 6
+    rng = np.random.default_rng(64016)
+    top = [56.0, 56.25, 2.0 ** -125, 0.0, 2.0 ** 100, 448.0 * 2.0 ** -117]  # block maxima
+    x = np.zeros((N, Dl), np.float32)
+    for b, a in enumerate(top):
+        if a == 0.0:
+            continue
+        if a < 2.0 ** -120:  # only 0 and normal values in the tiny block
+            blk = rng.choice([0.0, 2.0 ** -126, 1.5 * 2.0 ** -126], size=(64, Dl))
+        else:
+            blk = rng.uniform(-1, 1, (64, Dl)) * a
+            blk[np.abs(blk) < 2.0 ** -120] = 0.0  # no subnormal inputs
+        blk[rng.integers(64), rng.integers(Dl)] = -a
+        x[64 * b:64 * b + 64] = blk
+    lat_bits = synth.bf16_bits(x)
+    assert np.max(np.abs(on.bf16_to_f64(lat_bits[64:128]))) == 56.25  # the ulp above 56 survives bf16
+    rope_bits = synth.bf16_bits(rng.standard_normal((N, Dr)).astype(np.float32))
+    codes_d = torch.full((N, Dl), 0x7F, dtype=torch.uint8, device="cuda")
+    scales_d = torch.full((N // 64,), float("nan"), dtype=torch.float32, device="cuda")
+    rope_d = torch.zeros((N, Dr), dtype=torch.bfloat16, device="cuda")
+    slot = np.arange(N, dtype=np.int32)
+    _lib.pcp_kv_insert_fp8(dev_bf16(lat_bits), dev_bf16(rope_bits), torch.from_numpy(slot).cuda(), N, Dl, Dr, N,
+                           codes_d, rope_d, scales_d)
+    torch.cuda.synchronize()
+    codes_o, scales_o = ok.quantize_insert_fp8(np.full((N, Dl), 0x7F, np.uint8), np.full(N // 64, np.nan, np.float32),
+                                               lat_bits, slot)
+    want = np.array([2.0 ** -3, 2.0 ** -2, 2.0 ** -126, 1.0, 2.0 ** 92, 2.0 ** -117], np.float32)
+    assert np.array_equal(scales_o.view(np.uint32), want.view(np.uint32)), scales_o
+    got = scales_d.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), got
+    bad = np.argwhere(codes_d.cpu().numpy() != codes_o)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first {bad[:4].tolist()}"
+
+
 @pytest.mark.parametrize("dims", [(512, 64), (64, 16)])
 def test_fp8_insert_bit_exact(gpu_lib, dims):
     """Two insert calls on one cache: fresh blocks, a block opened by the first call and

@@ -354,13 +354,21 @@ __global__ __launch_bounds__(NTW, 1) void sparse_wide_kernel(
         // the wave's are powers of two the scaled conversion does the tile (the library's
         // quantiser writes such scales), else the multiply, with the same results
         float sc[NCH];
-        uint32_t odd = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            sc[c] = *reinterpret_cast<const float*>(st + ST_SCALE + 4 * ((c * NTW + tid) >> 5));
+        // pow2_scale of every one, as one test: no mantissa or sign bit in any, and the least
+        // and largest bit patterns (exponents) in range
+        uint32_t mant = 0, lo = ~0u, hi = 0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            sc[c] = *reinterpret_cast<const float*>(st + ST_SCALE + 4 * ((c * NTW + tid) >> 5));
-            odd |= pow2_scale(sc[c]) ? 0u : 1u;
+            const uint32_t b = __float_as_uint(sc[c]);
+            mant |= b & 0x807FFFFFu;
+            lo = min(lo, b);
+            hi = max(hi, b);
         }
-        const bool fast = __builtin_amdgcn_ballot_w64(odd != 0) == 0;  // wave-uniform
+        const bool p2 = mant == 0 && lo >= (10u << 23) && hi <= (246u << 23);
+        const bool fast = __builtin_amdgcn_ballot_w64(!p2) == 0;  // wave-uniform
         auto convert = [&](auto fast_tag) __attribute__((always_inline)) {
 #pragma unroll
             for (int b0 = 0; b0 < NCH; b0 += BATCH) {
